@@ -1,0 +1,222 @@
+"""CPU oracle for the compressed GDN/KDA recurrent-state decode update.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP library (``quantized_recurrent_state_02_amd``) and imports
+nothing from it.
+
+The arithmetic lives in ``qrs_oracle.c`` (FP32 as the pages fix it, plus an
+FP64 twin) and in ``model_f64.py`` (the model-space product form in FP64).
+This module only marshals numpy arrays into the C library.
+
+Sources: "DAMP: Decay-Aware Mixed-Precision Recurrent-State Quantization"
+(arXiv 2608.27513, HTML) and the reading notes on its v2; the functions below
+name the section or equation they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+DK = 128
+DV = 128
+KHI = 16
+KLO = DK - KHI
+GRP = 32
+NGRP = DV // GRP
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqrs_oracle.so")
+_lib = None
+
+
+def load():
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+
+        _build.build_oracle()
+    lib = ctypes.CDLL(LIB_PATH)
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_f16.restype = ctypes.c_uint16
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_f32.restype = ctypes.c_float
+    lib.orc_f32_to_f16_array.argtypes = [p, p, i64]
+    lib.orc_f16_to_f32_array.argtypes = [p, p, i64]
+    lib.orc_quantize_group.argtypes = [p, i, p, p]
+    lib.orc_store.argtypes = [p, p, p, i, p, p, p, i, p, i]
+    lib.orc_dequant.argtypes = [p, p, p, i, p, p, p, i, p, i]
+    lib.orc_i8_decode.argtypes = [p, p, p, i, p, p, p, i, i, p, p, p, p, p, p]
+    lib.orc_f32_decode.argtypes = [p, i, p, p, p, i, i, p, p, p, p, p, p]
+    lib.orc_f64_decode.argtypes = [p, i, p, p, p, i, i, p, p, p, p, p, p]
+    lib.orc_i8_prefill.argtypes = [p, p, p, i, p, p, p, i, i, i, p, p, p, p, p, p, i]
+    lib.orc_unit_bytes.argtypes = []
+    lib.orc_unit_bytes.restype = i64
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# FP16 and group codec
+# ---------------------------------------------------------------------------
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """IEEE binary16 round-to-nearest-even of FP32 values, as uint16 bits."""
+    x = _f32(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    load().orc_f32_to_f16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    load().orc_f16_to_f32_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def quantize_group(x: np.ndarray):
+    """Symmetric INT8 quantization of one group sharing one FP32 scale.
+
+    DAMP v2 reading notes, section 2.2, Eqs.(5)-(6): s = max|x|/127 and
+    code = round(x/s).  Returns (codes int8, scale float32).
+    """
+    x = _f32(x).ravel()
+    code = np.empty(x.size, dtype=np.int8)
+    s = np.empty(1, dtype=np.float32)
+    load().orc_quantize_group(_ptr(x), x.size, _ptr(code), _ptr(s))
+    return code, s[0]
+
+
+def unit_bytes() -> int:
+    return int(load().orc_unit_bytes())
+
+
+# ---------------------------------------------------------------------------
+# Pools
+# ---------------------------------------------------------------------------
+
+class OraclePool:
+    """Oracle representation of a packed state pool.
+
+    Unit u = slot * num_heads + head holds stored key rows 0..15 as FP16 bits
+    (``hi``), rows 16..127 as INT8 codes (``lo``) and one FP32 scale per 32
+    values of each INT8 row (``sc``) -- the DAMP packed representation
+    (arXiv HTML, Appendix A.5, Eq.(17)) with the v2 quantizer.
+    ``perm[h][i]`` is the model key channel stored in row i; ``c[h][j]`` the
+    value-column smoothing scale (v2 notes, section 2.7, Eq.(17) of v2).
+    """
+
+    def __init__(self, num_slots, num_heads, perm=None, c=None):
+        self.num_slots = num_slots
+        self.num_heads = num_heads
+        U = num_slots * num_heads
+        self.hi = np.zeros((U, KHI, DV), dtype=np.uint16)
+        self.lo = np.zeros((U, KLO, DV), dtype=np.int8)
+        self.sc = np.zeros((U, KLO, NGRP), dtype=np.float32)
+        self.perm = _i32(perm if perm is not None else np.tile(np.arange(DK), (num_heads, 1)))
+        self.c = _f32(c if c is not None else np.ones((num_heads, DV)))
+
+    def copy(self):
+        o = OraclePool.__new__(OraclePool)
+        o.num_slots, o.num_heads = self.num_slots, self.num_heads
+        o.hi, o.lo, o.sc = self.hi.copy(), self.lo.copy(), self.sc.copy()
+        o.perm, o.c = self.perm.copy(), self.c.copy()
+        return o
+
+    def store(self, slots, S, space=0):
+        """Encode states S [n][H][128][128]; space 0 = model, 1 = stored."""
+        slots = _i32(slots)
+        S = _f32(S)
+        load().orc_store(_ptr(self.hi), _ptr(self.lo), _ptr(self.sc), self.num_heads,
+                         _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, _ptr(S), space)
+
+    def dequant(self, slots, space=0):
+        slots = _i32(slots)
+        out = np.empty((slots.size, self.num_heads, DK, DV), dtype=np.float32)
+        load().orc_dequant(_ptr(self.hi), _ptr(self.lo), _ptr(self.sc), self.num_heads,
+                           _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, _ptr(out),
+                           space)
+        return out
+
+    def decode_step(self, slots, q, k, v, gate, beta, kind):
+        """One compressed decode step (kind 0 = GDN with alpha [n][H],
+        kind 1 = KDA with log-decay g [n][H][128]); returns o [n][H][128]."""
+        slots = _i32(slots)
+        q, k, v, gate, beta = (_f32(a) for a in (q, k, v, gate, beta))
+        o = np.empty((slots.size, self.num_heads, DV), dtype=np.float32)
+        load().orc_i8_decode(_ptr(self.hi), _ptr(self.lo), _ptr(self.sc), self.num_heads,
+                             _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, kind,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(o))
+        return o
+
+    def prefill(self, slots, q, k, v, alpha, beta, chunk, init_from_pool):
+        """Chunked prefill with GDN gating; q,k,v [n][T][H][128]."""
+        slots = _i32(slots)
+        q, k, v, alpha, beta = (_f32(a) for a in (q, k, v, alpha, beta))
+        n, T = q.shape[0], q.shape[1]
+        o = np.empty_like(q)
+        load().orc_i8_prefill(_ptr(self.hi), _ptr(self.lo), _ptr(self.sc), self.num_heads,
+                              _ptr(self.perm), _ptr(self.c), _ptr(slots), n, T, chunk,
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
+                              int(init_from_pool))
+        return o
+
+
+class OracleDensePool:
+    """Uncompressed state pool in stored coordinates, FP32 or FP64
+    (compression disabled)."""
+
+    def __init__(self, num_slots, num_heads, perm=None, c=None, dtype=np.float32):
+        self.num_slots = num_slots
+        self.num_heads = num_heads
+        self.dtype = np.dtype(dtype)
+        self.T = np.zeros((num_slots * num_heads, DK, DV), dtype=self.dtype)
+        self.perm = _i32(perm if perm is not None else np.tile(np.arange(DK), (num_heads, 1)))
+        self.c = _f32(c if c is not None else np.ones((num_heads, DV)))
+
+    def set_model(self, slots, S):
+        """Place model-space states S [n][H][128][128] (T = P_K S D_c^{-1})."""
+        for b, s in enumerate(np.asarray(slots)):
+            for h in range(self.num_heads):
+                Tm = np.asarray(S[b, h], dtype=np.float64 if self.dtype == np.float64 else np.float32)
+                Tm = Tm[self.perm[h], :] / self.c[h][None, :].astype(Tm.dtype)
+                self.T[s * self.num_heads + h] = Tm
+
+    def get_model(self, slots):
+        out = np.empty((len(slots), self.num_heads, DK, DV), dtype=self.dtype)
+        for b, s in enumerate(np.asarray(slots)):
+            for h in range(self.num_heads):
+                Tm = self.T[s * self.num_heads + h] * self.c[h][None, :].astype(self.dtype)
+                out[b, h][self.perm[h], :] = Tm
+        return out
+
+    def decode_step(self, slots, q, k, v, gate, beta, kind):
+        slots = _i32(slots)
+        q, k, v, gate, beta = (_f32(a) for a in (q, k, v, gate, beta))
+        o = np.empty((slots.size, self.num_heads, DV), dtype=self.dtype)
+        fn = load().orc_f64_decode if self.dtype == np.float64 else load().orc_f32_decode
+        fn(_ptr(self.T), self.num_heads, _ptr(self.perm), _ptr(self.c), _ptr(slots),
+           slots.size, kind, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(o))
+        return o
