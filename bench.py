@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark: compressed-state GDN / KDA decode on one MI355X.
+
+Metric: state updates per second and achieved HBM bandwidth (algorithmic
+bytes) against the MI355X peak, for GDN and KDA decode at batch 256,
+32 heads, d_k = d_v = 128.  A step is one decode step of all 256 x 32
+(slot, head) units through the fused kernel: packed-state load, dequantize,
+FP32 delta-rule update and readout, requantize, store.
+
+Algorithmic bytes per update (one unit advanced by one token):
+  state read 20,224 + state write 20,224 + q, k, v 3 x 512
+  + GDN alpha, beta 8  (= 41,992)   /  KDA g 512 + beta 4  (= 42,500).
+The FP32-state kernel on the same inputs moves 65,536 x 2 + 1,544 = 132,616.
+
+Inputs are the seeded synthetic workload (quantized_recurrent_state_02_amd/
+inputs.py), staged in device memory before the timed region.  The step loop
+is captured once in a HIP graph and replayed; HIP events on the launch
+stream bracket the timed replays.  By default 4 disjoint slot sets of 256
+requests are rotated step by step so the packed states (4 x 165.7 MB) exceed
+the 256 MB Infinity Cache and every state read comes from HBM; the
+single-pool figure is reported beside it.
+
+The CPU baseline is the oracle (oracle/, FP32 C code with OpenMP over units)
+timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+BYTES_GDN = 20224 * 2 + 3 * 512 + 8
+BYTES_KDA = 20224 * 2 + 3 * 512 + 512 + 4
+BYTES_F32_GDN = 65536 * 2 + 3 * 512 + 8
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gdn_b256_h32_counters.json")
+KERNEL_SOURCES = ["quantized_recurrent_state_02_amd/csrc/qrs_decode.hip",
+                  "quantized_recurrent_state_02_amd/csrc/qrs_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stage_inputs(torch, inputs, cfg, kind, n, H, steps):
+    """All per-step operands of `steps` steps, stacked on the device."""
+    t0 = time.time()
+    keys = ["q", "k", "v", "beta", "alpha" if kind == "gdn" else "g"]
+    host = {key: [] for key in keys}
+    for t in range(steps):
+        d = inputs.step_inputs(cfg, t, n, H, kind)
+        for key in keys:
+            host[key].append(d[key])
+    dev = {key: torch.from_numpy(np.stack(v)).to("cuda") for key, v in host.items()}
+    log(f"[bench] staged {steps} steps of {kind} inputs in {time.time() - t0:.1f}s")
+    return dev
+
+
+def time_loop(torch, launch, steps, warmup, use_graph):
+    """Run `launch(t)` for warmup + steps; return seconds for the timed steps."""
+    stream = torch.cuda.current_stream()
+    for t in range(warmup):
+        launch(t)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in range(warmup, warmup + steps):
+                launch(t)
+        torch.cuda.synchronize()
+        g.replay()                       # one untimed replay (graph upload)
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if use_graph:
+        g.replay()
+    else:
+        for t in range(warmup, warmup + steps):
+            launch(t)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def run_decode(torch, binding, inputs, kind, fmt, dev_in, perm, c, n, H, steps, warmup, pools,
+               use_graph):
+    total_slots = n * pools
+    pool = binding.StatePool(fmt, total_slots, H, perm, c)
+    cfg = 1 if kind == "gdn" else 2
+    S0 = inputs.initial_state(cfg, n, H)
+    S0d = torch.from_numpy(S0).to("cuda")
+    slot_sets = []
+    for p in range(pools):
+        s = torch.arange(p * n, (p + 1) * n, dtype=torch.int32, device="cuda")
+        pool.store(s, S0d)
+        slot_sets.append(s)
+    out = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
+    gate_key = "alpha" if kind == "gdn" else "g"
+    step_fn = pool.gdn_step if kind == "gdn" else pool.kda_step
+
+    def launch(t):
+        step_fn(slot_sets[t % pools], dev_in["q"][t], dev_in["k"][t], dev_in["v"][t],
+                dev_in[gate_key][t], dev_in["beta"][t], out)
+
+    secs = time_loop(torch, launch, steps, warmup, use_graph)
+    ok = bool(torch.isfinite(out).all().item())
+    pool.close()
+    del pool
+    torch.cuda.empty_cache()
+    return secs, ok
+
+
+def cpu_baseline(inputs, kind, budget_s=12.0):
+    """Oracle on a bounded sample: 64 slots x 32 heads, as many consecutive
+    steps as fit in about `budget_s` seconds (at least 2)."""
+    import oracle
+
+    cfg = 1 if kind == "gdn" else 2
+    n, H = 64, 32
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    op = oracle.OraclePool(n, H, perm, c)
+    slots = np.arange(n, dtype=np.int32)
+    op.store(slots, inputs.initial_state(cfg, n, H))
+    gate = "alpha" if kind == "gdn" else "g"
+    elapsed, steps = 0.0, 0
+    while steps < 256 and (elapsed < budget_s or steps < 2):
+        d = inputs.step_inputs(cfg, steps, n, H, kind)
+        t0 = time.perf_counter()
+        op.decode_step(slots, d["q"], d["k"], d["v"], d[gate], d["beta"], 0 if kind == "gdn" else 1)
+        elapsed += time.perf_counter() - t0
+        steps += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    ups = n * H * steps / elapsed
+    return {"value": ups, "unit": "state updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"{kind.upper()} decode, 64 slots x 32 heads x {steps} consecutive steps "
+                      f"({n * H * steps} updates, {elapsed:.1f} s of step-loop time)",
+            "gbs_algorithmic": ups * (BYTES_GDN if kind == "gdn" else BYTES_KDA) / 1e9}
+
+
+def traffic_from_profile(units):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, when
+    they were taken on the current kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=248)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--pools", type=int, default=4,
+                    help="slot sets rotated per step (4 = cache-cold working set)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["gdn", "kda", "f32", "all"], default="all")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not "
+                                   "part of this build (decode units shard by slot or head "
+                                   "with no exchange)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from quantized_recurrent_state_02_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    binding.load()
+    torch.cuda.set_device(0)
+    n, H = 256, 32
+    steps, warmup = args.steps, args.warmup
+    total = steps + warmup
+    use_graph = not args.no_graph
+    units = n * H
+    res = {}
+
+    if args.calib_copy_mb:
+        nb = args.calib_copy_mb << 20
+        a = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nb} bytes done (3 launches)")
+
+    perm1 = inputs.protected_perm(1, H)
+    c1 = inputs.smoothing(1, H, True)
+    if args.only in ("gdn", "f32", "all"):
+        gdn_in = stage_inputs(torch, inputs, 1, "gdn", n, H, total)
+        if args.only in ("gdn", "all"):
+            for pools in sorted({args.pools, 1}, reverse=True):
+                secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_I8F16, gdn_in,
+                                      perm1, c1, n, H, steps, warmup, pools, use_graph)
+                res[("gdn", pools)] = (secs, ok)
+                log(f"[bench] gdn pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        if args.only in ("f32", "all"):
+            secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_FP32, gdn_in, perm1,
+                                  c1, n, H, steps, warmup, 1, use_graph)
+            res[("f32", 1)] = (secs, ok)
+            log(f"[bench] fp32-state gdn: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        del gdn_in
+        torch.cuda.empty_cache()
+    if args.only in ("kda", "all"):
+        perm2 = inputs.protected_perm(2, H)
+        c2 = inputs.smoothing(2, H, True)
+        kda_in = stage_inputs(torch, inputs, 2, "kda", n, H, total)
+        for pools in sorted({args.pools, 1}, reverse=True):
+            secs, ok = run_decode(torch, binding, inputs, "kda", binding.FMT_I8F16, kda_in, perm2,
+                                  c2, n, H, steps, warmup, pools, use_graph)
+            res[("kda", pools)] = (secs, ok)
+            log(f"[bench] kda pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        del kda_in
+
+    def rate(key, nbytes):
+        secs, ok = res[key]
+        per_step = secs / steps
+        ups = units / per_step
+        return {"us_per_step": per_step * 1e6, "updates_per_s": ups,
+                "gbs": ups * nbytes / 1e9, "frac_of_peak": ups * nbytes / 1e9 / PEAK_HBM_GBS,
+                "finite_outputs": ok}
+
+    out = {}
+    head_key = ("gdn", args.pools) if ("gdn", args.pools) in res else next(iter(res))
+    kind0 = head_key[0]
+    nbytes0 = {"gdn": BYTES_GDN, "kda": BYTES_KDA, "f32": BYTES_F32_GDN}[kind0]
+    head = rate(head_key, nbytes0)
+    detail = {}
+    for key in res:
+        nb = {"gdn": BYTES_GDN, "kda": BYTES_KDA, "f32": BYTES_F32_GDN}[key[0]]
+        detail[f"{key[0]}_pools{key[1]}"] = rate(key, nb)
+    if ("gdn", 1) in res and ("f32", 1) in res:
+        detail["speedup_vs_fp32_state"] = res[("f32", 1)][0] / res[("gdn", 1)][0]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inputs, "gdn" if kind0 != "kda" else "kda")
+        log(f"[bench] cpu oracle: {cpu['value']:.3e} updates/s on {cpu['cores']} threads")
+
+    traffic = traffic_from_profile(units) if kind0 == "gdn" else None
+    out = {
+        "metric": "state updates/s + achieved HBM GB/s (% of peak), GDN/KDA decode B=256 H=32 d=128",
+        "value": head["updates_per_s"],
+        "unit": "state updates/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": head["us_per_step"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{kind0}_decode_compressed_state" if kind0 != "f32"
+                   else "gdn_decode_fp32_state",
+                   "batch": n, "heads": H, "d_k": 128, "d_v": 128,
+                   "state_format": "16 FP16 + 112 INT8 key rows, FP32 absmax/127 scale per 32",
+                   "slot_sets_rotated": args.pools if kind0 != "f32" else 1,
+                   "graph": use_graph,
+                   "bytes_per_update": nbytes0},
+        "hbm_gbs": head["gbs"],
+        "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": head["frac_of_peak"],
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "detail": detail,
+        "kernel_digest": kernel_digest(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * qrs.h -- C ABI of libqrs: compressed recurrent-state decode for Gated
+ * DeltaNet (GDN) and Kimi Delta Attention (KDA) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method follows "DAMP: Decay-Aware Mixed-Precision Recurrent-State
+ * Quantization" (arXiv 2608.27513; HTML version and the reading notes on its
+ * v2).  Each (request slot, head) state S in R^{128x128} (rows = key channels,
+ * columns = value dimensions) is kept in stored coordinates
+ *     T = P_K S D_c^{-1}                      (v2 notes, section 2.7, Eq.(17) of v2)
+ * i.e. stored row i holds model key channel perm[h][i] and value column j is
+ * divided by the smoothing scale c[h][j] > 0.  The first 16 stored rows are
+ * FP16, the other 112 are INT8 with one FP32 scale per 32 values
+ * (s = max|x| / 127, code = round-half-even(x / s), no zero point; v2 notes
+ * section 2.2, Eqs.(5)-(6)), packed contiguously per unit (HTML, Appendix A.5,
+ * Eq.(17)): 9.875 bits per state value (HTML, Eq.(12)).
+ *
+ * A decode step reads the packed state, dequantizes it, applies the
+ * delta-rule update in FP32
+ *     S_t = (I - beta k k^T) Lambda_t S_{t-1} + beta k v^T,  o_t = S_t^T q_t
+ * (HTML section 3.1, Eqs.(1)-(2); Lambda_t = alpha_t I for GDN,
+ * diag(exp(g_t)) for KDA), reads out from the FP32 state of this step, then
+ * recomputes the group scales, requantizes and writes back in place (v2 notes
+ * section 2.2; HTML Appendix A.5 "Fused decode executor").
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_host are host memory; every other pointer is HIP device
+ *    memory on the device that was current when the pool was created.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream);
+ *    inputs must stay valid and unmodified until the work completes.
+ *  - The caller owns all memory.  The library never allocates device memory;
+ *    it owns only the small host-side pool handle.
+ *  - Return value: QRS_OK, or a negative status (qrs_status_string names
+ *    it).  QRS_EINVAL: null pointer, negative size, bad enum, a perm that is
+ *    not a permutation, a non-positive or non-finite smoothing scale, a buffer
+ *    too small.  QRS_EUNSUPPORTED: a shape other than d_k = d_v = 128,
+ *    k_hi = 16, group = 32 (FP32 pools: k_hi = group = 0).  QRS_EDEVICE: a HIP
+ *    launch or copy failed (asynchronous faults surface at the caller's next
+ *    synchronization).  Nothing is enqueued when the call returns an error.
+ *  - Slot ids: int32 device array of length n.  Ids must be distinct within
+ *    one call (duplicates race on the same state).  A slot id outside
+ *    [0, num_slots) is skipped on the device: its state is not touched and
+ *    its output rows are filled with NaN.
+ *  - Operands are FP32, C-contiguous, in model key order; the library gathers
+ *    them through perm.  Calls on disjoint slots of one pool may overlap.
+ */
+#ifndef QRS_H
+#define QRS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct qrs_pool_s *qrs_pool;
+
+/* Pool formats. */
+enum {
+    QRS_FMT_FP32 = 0,  /* uncompressed FP32 state (compression disabled) */
+    QRS_FMT_I8F16 = 1  /* 16 FP16 rows + 112 INT8 rows, FP32 scale per 32 values */
+};
+
+/* Coordinate spaces for store / dequant. */
+enum {
+    QRS_SPACE_MODEL = 0,  /* S in model key order, unsmoothed */
+    QRS_SPACE_STORED = 1  /* T = P_K S D_c^{-1}, stored row order */
+};
+
+/* Status codes. */
+enum {
+    QRS_OK = 0,
+    QRS_EINVAL = -1,
+    QRS_EUNSUPPORTED = -2,
+    QRS_EDEVICE = -3
+};
+
+/*
+ * Layout of one unit u = slot * num_heads + head, at byte offset
+ * u * unit_bytes from the pool base (unit_bytes is a multiple of 256):
+ *   QRS_FMT_I8F16 (20224 bytes):
+ *     [0, 4096)       FP16 rows 0..15, row-major [16][128] (IEEE binary16 bits)
+ *     [4096, 18432)   INT8 codes of rows 16..127, row-major [112][128]
+ *     [18432, 20224)  FP32 scales [112][4]; scale g of a row covers
+ *                     columns 32g..32g+31
+ *   QRS_FMT_FP32 (65536 bytes): FP32 [128][128] row-major.
+ * After the num_slots * num_heads units: perm int32 [H][128] and c FP32
+ * [H][128], each starting on a 256-byte boundary.
+ */
+#define QRS_I8F16_UNIT_BYTES 20224
+#define QRS_I8F16_HI_OFFSET 0
+#define QRS_I8F16_LO_OFFSET 4096
+#define QRS_I8F16_SCALE_OFFSET 18432
+#define QRS_FP32_UNIT_BYTES 65536
+
+/*
+ * Bytes of device memory a pool needs (state units plus the perm / smoothing
+ * tail).  Returns 0 for an invalid or unsupported shape.
+ */
+size_t qrs_state_pool_bytes(int fmt, int num_slots, int num_heads, int d_k, int d_v, int k_hi,
+                            int group);
+
+/*
+ * Create a pool over caller-owned device memory `dev_mem` of `dev_bytes`
+ * (>= qrs_state_pool_bytes(...), 256-byte aligned).  Copies perm_host
+ * ([H][128], stored row i <- model key channel perm_host[h][i]; NULL =
+ * identity) and smooth_host ([H][128], c > 0; NULL = ones) into the pool tail
+ * and zero-fills the state region (the tables synchronously, the fill on
+ * `stream`).  FP32 pools hold the state uncompressed in the same stored
+ * coordinates (compression disabled).  The key permutation is a
+ * static per-head layout stored once with the model (HTML section 5.2 and
+ * Appendix A.5); smoothing is the per-value-column scaling of v2 (notes
+ * section 2.7).  On success *out receives the handle.
+ */
+int qrs_create_state_pool(int fmt, int num_slots, int num_heads, int d_k, int d_v, int k_hi,
+                          int group, void *dev_mem, size_t dev_bytes, const int32_t *perm_host,
+                          const float *smooth_host, hipStream_t stream, qrs_pool *out);
+
+/* Release the host handle (the device memory stays the caller's).  NULL is a no-op. */
+int qrs_destroy_state_pool(qrs_pool pool);
+
+/* Geometry of a pool: any output pointer may be NULL. */
+int qrs_pool_info(qrs_pool pool, int *fmt, int *num_slots, int *num_heads, size_t *unit_bytes,
+                  size_t *perm_offset, size_t *smooth_offset);
+
+/*
+ * Write states into the given slots.  S: FP32 [n][H][128][128].
+ * space QRS_SPACE_MODEL: T[i][j] = S[perm[i]][j] / c[j] (IEEE FP32 divide),
+ * then encode; QRS_SPACE_STORED: S is already T.  Encoding: rows 0..15
+ * FP16 round-to-nearest-even; rows 16..127 per 32-value group
+ * s = RN(amax / 127) and code = RN_int(RN(x / s)), s = 0 and codes 0 when
+ * the scale is zero (v2 notes section 2.2, Eqs.(5)-(6)).  FP32 pools copy.
+ */
+int qrs_store_state(qrs_pool pool, const int32_t *slots, int n, const float *S, int space,
+                    hipStream_t stream);
+
+/*
+ * Read states back.  S_out: FP32 [n][H][128][128].  Dequantization is
+ * T = f32(fp16) on rows 0..15 and T = s * f32(code) on rows 16..127 (v2 notes
+ * section 2.2, Eq.(6)); QRS_SPACE_MODEL then writes S[perm[i]][j] = T[i][j] * c[j].
+ */
+int qrs_dequant_state(qrs_pool pool, const int32_t *slots, int n, float *S_out, int space,
+                      hipStream_t stream);
+
+/*
+ * One GDN decode step on n slots x H heads, in place (HTML section 3.1,
+ * Eq.(1), Lambda = alpha I):
+ *   q, k, v: FP32 [n][H][128] in model order; alpha, beta: FP32 [n][H];
+ *   o: FP32 [n][H][128] output, model value order, o = S_t^T q from the FP32
+ *   state of this step before requantization.
+ * Compressed pools: dequantize -> FP32 update and readout -> requantize
+ * (one fused kernel); FP32 pools: the same update on the FP32 state.
+ */
+int qrs_gdn_decode_step(qrs_pool pool, const int32_t *slots, int n, const float *q,
+                        const float *k, const float *v, const float *alpha, const float *beta,
+                        float *o, hipStream_t stream);
+
+/*
+ * One KDA decode step: as qrs_gdn_decode_step with per-key-channel decay
+ * Lambda = diag(exp(g)) (HTML section 3.1); g: FP32 [n][H][128] log-decay in
+ * model key order (exp is evaluated on the device).
+ */
+int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float *q,
+                        const float *k, const float *v, const float *g, const float *beta,
+                        float *o, hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char *qrs_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QRS_H */

@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libqrs (include/qrs.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, torch
+tensors are turned into device pointers and the current torch stream is
+passed as the hipStream_t.  Every step of the computation runs in the HIP
+library; there is no fallback.  Importing torch first makes the library bind
+to the HIP runtime torch already loaded.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqrs.so")
+
+FMT_FP32 = 0
+FMT_I8F16 = 1
+SPACE_MODEL = 0
+SPACE_STORED = 1
+OK = 0
+DK = DV = 128
+KHI = 16
+GRP = 32
+UNIT_BYTES = {FMT_FP32: 65536, FMT_I8F16: 20224}
+HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
+
+EXPORTED = (
+    "qrs_state_pool_bytes", "qrs_create_state_pool", "qrs_destroy_state_pool", "qrs_pool_info",
+    "qrs_store_state", "qrs_dequant_state", "qrs_gdn_decode_step", "qrs_kda_decode_step",
+    "qrs_status_string",
+)
+
+_lib = None
+
+
+class QrsError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load libqrs.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise QrsError(f"{path} is missing: build it with __graft_entry__.build() "
+                       "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.qrs_state_pool_bytes.argtypes = [i] * 7
+    lib.qrs_state_pool_bytes.restype = sz
+    lib.qrs_create_state_pool.argtypes = [i] * 7 + [p, sz, p, p, p, ctypes.POINTER(p)]
+    lib.qrs_create_state_pool.restype = i
+    lib.qrs_destroy_state_pool.argtypes = [p]
+    lib.qrs_destroy_state_pool.restype = i
+    lib.qrs_pool_info.argtypes = [p] + [ctypes.POINTER(i)] * 3 + [ctypes.POINTER(sz)] * 3
+    lib.qrs_pool_info.restype = i
+    lib.qrs_store_state.argtypes = [p, p, i, p, i, p]
+    lib.qrs_store_state.restype = i
+    lib.qrs_dequant_state.argtypes = [p, p, i, p, i, p]
+    lib.qrs_dequant_state.restype = i
+    for name in ("qrs_gdn_decode_step", "qrs_kda_decode_step"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, i, p, p, p, p, p, p, p]
+        fn.restype = i
+    lib.qrs_status_string.argtypes = [i]
+    lib.qrs_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        msg = load().qrs_status_string(status).decode()
+        raise QrsError(f"{what}: {msg} ({status})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, shape, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise QrsError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise QrsError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise QrsError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise QrsError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pool_bytes(fmt: int, num_slots: int, num_heads: int) -> int:
+    khi, grp = (KHI, GRP) if fmt == FMT_I8F16 else (0, 0)
+    return int(load().qrs_state_pool_bytes(fmt, num_slots, num_heads, DK, DV, khi, grp))
+
+
+class StatePool:
+    """A packed state pool in device memory owned by a torch uint8 tensor."""
+
+    def __init__(self, fmt: int, num_slots: int, num_heads: int, perm=None, smooth=None,
+                 device="cuda"):
+        lib = load()
+        self.fmt, self.num_slots, self.num_heads = fmt, num_slots, num_heads
+        nbytes = pool_bytes(fmt, num_slots, num_heads)
+        if nbytes == 0:
+            raise QrsError("unsupported pool shape")
+        self.mem = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self._perm = None if perm is None else np.ascontiguousarray(perm, dtype=np.int32)
+        self._smooth = None if smooth is None else np.ascontiguousarray(smooth, dtype=np.float32)
+        for arr, shape, name in ((self._perm, (num_heads, DK), "perm"),
+                                 (self._smooth, (num_heads, DV), "smooth")):
+            if arr is not None and arr.shape != shape:
+                raise QrsError(f"{name} must have shape {shape}")
+        handle = ctypes.c_void_p()
+        khi, grp = (KHI, GRP) if fmt == FMT_I8F16 else (0, 0)
+        st = lib.qrs_create_state_pool(
+            fmt, num_slots, num_heads, DK, DV, khi, grp, ctypes.c_void_p(self.mem.data_ptr()),
+            nbytes,
+            None if self._perm is None else self._perm.ctypes.data_as(ctypes.c_void_p),
+            None if self._smooth is None else self._smooth.ctypes.data_as(ctypes.c_void_p),
+            _stream(), ctypes.byref(handle))
+        _check(st, "qrs_create_state_pool")
+        self.handle = handle
+        self.unit_bytes = UNIT_BYTES[fmt]
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load().qrs_destroy_state_pool(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- raw views (for checks and export) --
+    def units(self) -> torch.Tensor:
+        """The state region as uint8 [num_slots * H][unit_bytes] (a view)."""
+        n = self.num_slots * self.num_heads * self.unit_bytes
+        return self.mem[:n].view(self.num_slots * self.num_heads, self.unit_bytes)
+
+    def store(self, slots: torch.Tensor, S: torch.Tensor, space: int = SPACE_MODEL):
+        n = slots.numel()
+        st = load().qrs_store_state(self.handle, _dev(slots, torch.int32, (n,), "slots"), n,
+                                    _dev(S, torch.float32, (n, self.num_heads, DK, DV), "S"),
+                                    space, _stream())
+        _check(st, "qrs_store_state")
+
+    def dequant(self, slots: torch.Tensor, space: int = SPACE_MODEL, out=None) -> torch.Tensor:
+        n = slots.numel()
+        if out is None:
+            out = torch.empty((n, self.num_heads, DK, DV), dtype=torch.float32,
+                              device=self.mem.device)
+        st = load().qrs_dequant_state(self.handle, _dev(slots, torch.int32, (n,), "slots"), n,
+                                      _dev(out, torch.float32, (n, self.num_heads, DK, DV), "out"),
+                                      space, _stream())
+        _check(st, "qrs_dequant_state")
+        return out
+
+    def _step(self, fn, name, slots, q, k, v, gate, gate_shape, beta, out):
+        n, H = slots.numel(), self.num_heads
+        if out is None:
+            out = torch.empty((n, H, DV), dtype=torch.float32, device=self.mem.device)
+        st = fn(self.handle, _dev(slots, torch.int32, (n,), "slots"), n,
+                _dev(q, torch.float32, (n, H, DK), "q"), _dev(k, torch.float32, (n, H, DK), "k"),
+                _dev(v, torch.float32, (n, H, DV), "v"), _dev(gate, torch.float32, gate_shape, "gate"),
+                _dev(beta, torch.float32, (n, H), "beta"),
+                _dev(out, torch.float32, (n, H, DV), "o"), _stream())
+        _check(st, name)
+        return out
+
+    def gdn_step(self, slots, q, k, v, alpha, beta, out=None):
+        n = slots.numel()
+        return self._step(load().qrs_gdn_decode_step, "qrs_gdn_decode_step", slots, q, k, v,
+                          alpha, (n, self.num_heads), beta, out)
+
+    def kda_step(self, slots, q, k, v, g, beta, out=None):
+        n = slots.numel()
+        return self._step(load().qrs_kda_decode_step, "qrs_kda_decode_step", slots, q, k, v, g,
+                          (n, self.num_heads, DK), beta, out)
+
+
+def split_units(raw: np.ndarray):
+    """Split packed I8F16 unit bytes [U][20224] into (hi uint16 [U][16][128],
+    lo int8 [U][112][128], sc float32 [U][112][4]) per the layout in qrs.h."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    U = raw.shape[0]
+    hi = raw[:, HI_OFFSET:LO_OFFSET].copy().view(np.uint16).reshape(U, KHI, DV)
+    lo = raw[:, LO_OFFSET:SCALE_OFFSET].copy().view(np.int8).reshape(U, DK - KHI, DV)
+    sc = raw[:, SCALE_OFFSET:].copy().view(np.float32).reshape(U, DK - KHI, DV // GRP)
+    return hi, lo, sc

@@ -1,0 +1,243 @@
+// qrs_api.hip -- the C ABI declared in include/qrs.h: argument validation,
+// pool handles and kernel launches.  Every check happens on the host before
+// anything is enqueued, so an error return leaves the stream untouched.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/qrs.h"
+#include "qrs_internal.h"
+
+namespace qrs {
+hipError_t launch_decode_i8f16(int kind, const PoolView &pool, const int32_t *slots, int n,
+                               const float *q, const float *k, const float *v, const float *gate,
+                               const float *beta, float *o, hipStream_t stream);
+hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n,
+                             const float *q, const float *k, const float *v, const float *gate,
+                             const float *beta, float *o, hipStream_t stream);
+hipError_t launch_store(int fmt, const PoolView &pool, const int32_t *slots, int n, const float *S,
+                        int space, hipStream_t stream);
+hipError_t launch_dequant(int fmt, const PoolView &pool, const int32_t *slots, int n, float *S,
+                          int space, hipStream_t stream);
+}  // namespace qrs
+
+struct qrs_pool_s {
+    int fmt;
+    int num_slots;
+    int num_heads;
+    size_t unit_bytes;
+    size_t perm_offset;
+    size_t smooth_offset;
+    size_t total_bytes;
+    uint8_t *base;
+    int device;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool shape_ok(int fmt, int d_k, int d_v, int k_hi, int group) {
+    if (d_k != qrs::DK || d_v != qrs::DV) return false;
+    if (fmt == QRS_FMT_I8F16) return k_hi == qrs::KHI && group == qrs::GRP;
+    if (fmt == QRS_FMT_FP32) return k_hi == 0 && group == 0;
+    return false;
+}
+
+// Layout of a pool; returns false for invalid sizes.
+bool layout(int fmt, int num_slots, int num_heads, size_t *unit_bytes, size_t *perm_off,
+            size_t *smooth_off, size_t *total) {
+    if (num_slots <= 0 || num_heads <= 0) return false;
+    const size_t ub = fmt == QRS_FMT_I8F16 ? (size_t)qrs::UNIT_BYTES : (size_t)qrs::F32_UNIT_BYTES;
+    const size_t units = (size_t)num_slots * (size_t)num_heads;
+    if (units > ((size_t)1 << 40) / ub) return false;
+    const size_t meta = round_up((size_t)num_heads * qrs::DK * sizeof(int32_t));
+    *unit_bytes = ub;
+    *perm_off = round_up(units * ub);
+    *smooth_off = *perm_off + meta;
+    *total = *smooth_off + round_up((size_t)num_heads * qrs::DV * sizeof(float));
+    return true;
+}
+
+qrs::PoolView view(const qrs_pool_s *p) {
+    qrs::PoolView v;
+    v.base = p->base;
+    v.perm = reinterpret_cast<const int32_t *>(p->base + p->perm_offset);
+    v.smooth = reinterpret_cast<const float *>(p->base + p->smooth_offset);
+    v.num_slots = p->num_slots;
+    v.num_heads = p->num_heads;
+    return v;
+}
+
+// Launches must happen with the pool's device current.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            ok = false;
+            return;
+        }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+int decode_common(int kind, qrs_pool pool, const int32_t *slots, int n, const float *q,
+                  const float *k, const float *v, const float *gate, const float *beta, float *o,
+                  hipStream_t stream) {
+    if (!pool || n < 0) return QRS_EINVAL;
+    if (n == 0) return QRS_OK;
+    if (!slots || !q || !k || !v || !gate || !beta || !o) return QRS_EINVAL;
+    if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu) return QRS_EINVAL;
+    DeviceGuard g(pool->device);
+    if (!g.ok) return QRS_EDEVICE;
+    const qrs::PoolView pv = view(pool);
+    hipError_t e = pool->fmt == QRS_FMT_I8F16
+                       ? qrs::launch_decode_i8f16(kind, pv, slots, n, q, k, v, gate, beta, o, stream)
+                       : qrs::launch_decode_f32(kind, pv, slots, n, q, k, v, gate, beta, o, stream);
+    return e == hipSuccess ? QRS_OK : QRS_EDEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qrs_state_pool_bytes(int fmt, int num_slots, int num_heads, int d_k, int d_v, int k_hi,
+                            int group) {
+    if (!shape_ok(fmt, d_k, d_v, k_hi, group)) return 0;
+    size_t ub, po, so, total;
+    if (!layout(fmt, num_slots, num_heads, &ub, &po, &so, &total)) return 0;
+    return total;
+}
+
+int qrs_create_state_pool(int fmt, int num_slots, int num_heads, int d_k, int d_v, int k_hi,
+                          int group, void *dev_mem, size_t dev_bytes, const int32_t *perm_host,
+                          const float *smooth_host, hipStream_t stream, qrs_pool *out) {
+    if (!out) return QRS_EINVAL;
+    *out = nullptr;
+    if (fmt != QRS_FMT_FP32 && fmt != QRS_FMT_I8F16) return QRS_EINVAL;
+    if (!shape_ok(fmt, d_k, d_v, k_hi, group)) return QRS_EUNSUPPORTED;
+    size_t ub, po, so, total;
+    if (!layout(fmt, num_slots, num_heads, &ub, &po, &so, &total)) return QRS_EINVAL;
+    if (!dev_mem || dev_bytes < total) return QRS_EINVAL;
+    if (reinterpret_cast<uintptr_t>(dev_mem) % kAlign != 0) return QRS_EINVAL;
+
+    std::vector<int32_t> perm((size_t)num_heads * qrs::DK);
+    std::vector<float> smooth((size_t)num_heads * qrs::DV);
+    for (int h = 0; h < num_heads; ++h) {
+        std::vector<char> seen(qrs::DK, 0);
+        for (int i = 0; i < qrs::DK; ++i) {
+            const int32_t p = perm_host ? perm_host[(size_t)h * qrs::DK + i] : i;
+            if (p < 0 || p >= qrs::DK || seen[p]) return QRS_EINVAL;
+            seen[p] = 1;
+            perm[(size_t)h * qrs::DK + i] = p;
+        }
+        for (int j = 0; j < qrs::DV; ++j) {
+            const float c = smooth_host ? smooth_host[(size_t)h * qrs::DV + j] : 1.0f;
+            if (!(c > 0.0f) || !std::isfinite(c)) return QRS_EINVAL;
+            smooth[(size_t)h * qrs::DV + j] = c;
+        }
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QRS_EDEVICE;
+    qrs_pool_s *p = new (std::nothrow) qrs_pool_s;
+    if (!p) return QRS_EDEVICE;
+    p->fmt = fmt;
+    p->num_slots = num_slots;
+    p->num_heads = num_heads;
+    p->unit_bytes = ub;
+    p->perm_offset = po;
+    p->smooth_offset = so;
+    p->total_bytes = total;
+    p->base = static_cast<uint8_t *>(dev_mem);
+    p->device = dev;
+    // Synchronous copies of the small tables (the host vectors die on return),
+    // then the state region is zero-filled on the caller's stream.
+    if (hipMemcpy(p->base + po, perm.data(), perm.size() * sizeof(int32_t),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(p->base + so, smooth.data(), smooth.size() * sizeof(float),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemsetAsync(p->base, 0, po, stream) != hipSuccess) {
+        delete p;
+        return QRS_EDEVICE;
+    }
+    *out = p;
+    return QRS_OK;
+}
+
+int qrs_destroy_state_pool(qrs_pool pool) {
+    delete pool;
+    return QRS_OK;
+}
+
+int qrs_pool_info(qrs_pool pool, int *fmt, int *num_slots, int *num_heads, size_t *unit_bytes,
+                  size_t *perm_offset, size_t *smooth_offset) {
+    if (!pool) return QRS_EINVAL;
+    if (fmt) *fmt = pool->fmt;
+    if (num_slots) *num_slots = pool->num_slots;
+    if (num_heads) *num_heads = pool->num_heads;
+    if (unit_bytes) *unit_bytes = pool->unit_bytes;
+    if (perm_offset) *perm_offset = pool->perm_offset;
+    if (smooth_offset) *smooth_offset = pool->smooth_offset;
+    return QRS_OK;
+}
+
+int qrs_store_state(qrs_pool pool, const int32_t *slots, int n, const float *S, int space,
+                    hipStream_t stream) {
+    if (!pool || n < 0 || (space != QRS_SPACE_MODEL && space != QRS_SPACE_STORED))
+        return QRS_EINVAL;
+    if (n == 0) return QRS_OK;
+    if (!slots || !S) return QRS_EINVAL;
+    if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu) return QRS_EINVAL;
+    DeviceGuard g(pool->device);
+    if (!g.ok) return QRS_EDEVICE;
+    return qrs::launch_store(pool->fmt, view(pool), slots, n, S, space, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
+}
+
+int qrs_dequant_state(qrs_pool pool, const int32_t *slots, int n, float *S_out, int space,
+                      hipStream_t stream) {
+    if (!pool || n < 0 || (space != QRS_SPACE_MODEL && space != QRS_SPACE_STORED))
+        return QRS_EINVAL;
+    if (n == 0) return QRS_OK;
+    if (!slots || !S_out) return QRS_EINVAL;
+    if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu) return QRS_EINVAL;
+    DeviceGuard g(pool->device);
+    if (!g.ok) return QRS_EDEVICE;
+    return qrs::launch_dequant(pool->fmt, view(pool), slots, n, S_out, space, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
+}
+
+int qrs_gdn_decode_step(qrs_pool pool, const int32_t *slots, int n, const float *q,
+                        const float *k, const float *v, const float *alpha, const float *beta,
+                        float *o, hipStream_t stream) {
+    return decode_common(0, pool, slots, n, q, k, v, alpha, beta, o, stream);
+}
+
+int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float *q,
+                        const float *k, const float *v, const float *g, const float *beta,
+                        float *o, hipStream_t stream) {
+    return decode_common(1, pool, slots, n, q, k, v, g, beta, o, stream);
+}
+
+const char *qrs_status_string(int status) {
+    switch (status) {
+    case QRS_OK: return "QRS_OK";
+    case QRS_EINVAL: return "QRS_EINVAL: invalid argument";
+    case QRS_EUNSUPPORTED: return "QRS_EUNSUPPORTED: unsupported shape or format";
+    case QRS_EDEVICE: return "QRS_EDEVICE: HIP runtime error";
+    default: return "unknown qrs status";
+    }
+}
+
+}  // extern "C"
