@@ -132,12 +132,13 @@ def run_decode(torch, binding, inputs, kind, fmt, dev_in, perm, c, n, H, steps, 
 
 
 def cpu_baseline(inputs, kind, budget_s=12.0):
-    """Oracle on a bounded sample: 64 slots x 32 heads, as many consecutive
-    steps as fit in about `budget_s` seconds (at least 2)."""
+    """Oracle on a bounded sample of the same workload: all 256 slots x 32
+    heads, the first consecutive steps that fit in about `budget_s` seconds
+    of step-loop time (at least 2)."""
     import oracle
 
     cfg = 1 if kind == "gdn" else 2
-    n, H = 64, 32
+    n, H = 256, 32
     perm = inputs.protected_perm(cfg, H)
     c = inputs.smoothing(cfg, H, True)
     op = oracle.OraclePool(n, H, perm, c)
@@ -154,7 +155,7 @@ def cpu_baseline(inputs, kind, budget_s=12.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     ups = n * H * steps / elapsed
     return {"value": ups, "unit": "state updates/s", "cores": threads, "kind": "oracle",
-            "sample": f"{kind.upper()} decode, 64 slots x 32 heads x {steps} consecutive steps "
+            "sample": f"{kind.upper()} decode, {n} slots x {H} heads x {steps} consecutive steps "
                       f"({n * H * steps} updates, {elapsed:.1f} s of step-loop time)",
             "gbs_algorithmic": ups * (BYTES_GDN if kind == "gdn" else BYTES_KDA) / 1e9}
 

@@ -75,15 +75,13 @@ __global__ __launch_bounds__(THREADS) void store_i8f16_kernel(PoolView pool,
         amax = fmaxf(amax, partner_xor1(amax));
         const float s = group_scale(amax);
         const double rinv = scale_reciprocal(s);
-        uint32_t cw[4];
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
-            cw[c4] = pack4_low_bytes(quant_code_bits(x[r][4 * c4], rinv),
-                                     quant_code_bits(x[r][4 * c4 + 1], rinv),
-                                     quant_code_bits(x[r][4 * c4 + 2], rinv),
-                                     quant_code_bits(x[r][4 * c4 + 3], rinv));
+        V4 cw;
+        cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
+        cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
+        cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
+        cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
         const int lrow = rg + 16 * (r - 1);
-        *reinterpret_cast<V4 *>(unit + LO_OFF + lrow * DV + cb * 16) = V4{cw[0], cw[1], cw[2], cw[3]};
+        *reinterpret_cast<V4 *>(unit + LO_OFF + lrow * DV + cb * 16) = cw;
         if ((cb & 1) == 0)
             *reinterpret_cast<float *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4) = s;
     }

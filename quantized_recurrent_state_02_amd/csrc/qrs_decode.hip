@@ -13,27 +13,26 @@
 // The state never leaves registers between the load and the store.  Operands
 // arrive in model key order and are gathered through the per-head
 // permutation; v is divided by the smoothing scales c and the readout is
-// multiplied by them (v2 notes, section 2.7).
+// multiplied by them (v2 notes, section 2.7).  The readout uses
+// z + (q'.k') beta delta = T^T q' (the FP32 state of this step before
+// requantization), so both column reductions run in one pass before the
+// update.
 //
-// The readout uses z + (q'.k') beta delta = T^T q' (the post-update FP32
-// state of this step, before requantization), so both column reductions run
-// in the same pass before the update.
+// Cost model (gfx950): every byte of the unit is read once and written once
+// with 128-bit buffer accesses (non-temporal, except the FP16-row stores, see
+// below).  The VALU work is about eleven instructions per state value:
+// convert, scale, two reduction FMAs, the update FMA, half an absmax, a
+// four-instruction exact quantizer whose last step also packs the code byte,
+// and per-row / per-unit overheads.  Four workgroups fit per CU (176 VGPRs);
+// the grid is one workgroup per unit, so the hardware refills CUs as units
+// finish.  Persistent workgroups that prefetch their next unit into registers
+// measured slower: loads and stores share one wait counter on gfx9, so every
+// iteration also waited for the previous unit's stores.
 #include "qrs_internal.h"
 
 namespace qrs {
 
 namespace {
-
-struct alignas(16) U4 {
-    uint32_t x, y, z, w;
-};
-
-__device__ __forceinline__ U4 ld16(const uint8_t *p) {
-    return *reinterpret_cast<const U4 *>(p);
-}
-__device__ __forceinline__ void st16(uint8_t *p, U4 v) {
-    *reinterpret_cast<U4 *>(p) = v;
-}
 
 // Sum over the 64 lanes of a wave (every lane gets the total).
 __device__ __forceinline__ float wave_sum(float x) {
@@ -70,37 +69,39 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
     }
     const int cb = tid & 7;
     const int rg = tid >> 3;
-    uint8_t *unit = pool.base + ((size_t)slot * H + h) * UNIT_BYTES;
+    const __amdgpu_buffer_rsrc_t st =
+        make_rsrc(pool.base + ((size_t)slot * H + h) * UNIT_BYTES, UNIT_BYTES);
+    // Byte offsets of this thread's pieces: FP16 row rg (32 B at off_hi); INT8
+    // row rg + 16 (r - 1) (16 B at off_lo + LO_OFF + 2048 (r - 1)) and its
+    // scale (off_sc + SC_OFF + 256 (r - 1)).
+    const int off_hi = HI_OFF + rg * (DV * 2) + cb * 32;
+    const int off_lo = rg * DV + cb * 16;
+    const int off_sc = (rg * NGRP + (cb >> 1)) * 4;
 
     // ---- issue the state loads first (the long-latency part) ----
     U4 hi_raw[2];
     U4 lo_raw[ROWS_PER_THREAD - 1];
     float sc_old[ROWS_PER_THREAD - 1];
-    {
-        const uint8_t *hp = unit + HI_OFF + rg * (DV * 2) + cb * 32;
-        hi_raw[0] = ld16(hp);
-        hi_raw[1] = ld16(hp + 16);
+    hi_raw[0] = buf_load16(st, off_hi, 0);
+    hi_raw[1] = buf_load16(st, off_hi + 16, 0);
 #pragma unroll
-        for (int r = 1; r < ROWS_PER_THREAD; ++r) {
-            const int lrow = rg + 16 * (r - 1);  // INT8 row index 0..111
-            lo_raw[r - 1] = ld16(unit + LO_OFF + lrow * DV + cb * 16);
-            sc_old[r - 1] =
-                *reinterpret_cast<const float *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4);
-        }
+    for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+        lo_raw[r - 1] = buf_load16(st, off_lo, LO_OFF + 2048 * (r - 1));
+        sc_old[r - 1] = buf_loadf(st, off_sc + 256 * (r - 1), SC_OFF);
     }
 
     // ---- operands: thread t gathers stored row t and owns value column t ----
     const size_t ob = (size_t)uu * DK;
     const int src = pool.perm[h * DK + tid];
-    const float kt = k[ob + src];
-    const float qt = q[ob + src];
+    const float kt = buf_loadf(make_rsrc(k + ob, DK * 4), src * 4, 0);
+    const float qt = buf_loadf(make_rsrc(q + ob, DK * 4), src * 4, 0);
     float dec_t;
     if (KIND == 0)
         dec_t = gate[uu];
     else
-        dec_t = expf(gate[ob + src]);
+        dec_t = expf(buf_loadf(make_rsrc(gate + ob, DK * 4), src * 4, 0));
     const float c_t = pool.smooth[h * DV + tid];
-    const float vp_t = v[ob + tid] / c_t;  // v' = D_c^{-1} v
+    const float vp_t = __builtin_nontemporal_load(v + ob + tid) / c_t;  // v' = D_c^{-1} v
     const float beta_u = beta[uu];
     s_k[tid] = kt;
     s_q[tid] = qt;
@@ -139,11 +140,14 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
         for (int c = 0; c < 16; ++c) x[r][c] = a * sext_byte_to_f32(lw[c >> 2], c & 3);
     }
 
-    // ---- partial column reductions over this thread's 8 rows ----
-    {
-        float pw[COLS_PER_THREAD], pz[COLS_PER_THREAD];
+    // ---- partial column reductions over this thread's 8 rows, written to
+    //      LDS four columns at a time ----
 #pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) {
+    for (int c4 = 0; c4 < 4; ++c4) {
+        float pw[4], pz[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * c4 + j;
             float aw = kr[0] * x[0][c];
             float az = qr[0] * x[0][c];
 #pragma unroll
@@ -151,16 +155,11 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
                 aw = __builtin_fmaf(kr[r], x[r][c], aw);
                 az = __builtin_fmaf(qr[r], x[r][c], az);
             }
-            pw[c] = aw;
-            pz[c] = az;
+            pw[j] = aw;
+            pz[j] = az;
         }
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            red_w[rg][cb * 4 + c4] =
-                make_float4(pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]);
-            red_z[rg][cb * 4 + c4] =
-                make_float4(pz[4 * c4], pz[4 * c4 + 1], pz[4 * c4 + 2], pz[4 * c4 + 3]);
-        }
+        red_w[rg][cb * 4 + c4] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+        red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
     }
     __syncthreads();
 
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
         const float delta = vp_t - w;
         const float bd = beta_u * delta;
         const float qk = s_qk[0] + s_qk[1];
-        o[(size_t)uu * DV + tid] = c_t * __builtin_fmaf(qk, bd, z);
+        __builtin_nontemporal_store(c_t * __builtin_fmaf(qk, bd, z), o + (size_t)uu * DV + tid);
         s_bd[tid] = bd;
     }
     __syncthreads();
@@ -186,20 +185,23 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
 #pragma unroll
     for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb * 16 + c];
 
-    // ---- rank-1 write, requantize, store ----
-    // FP16 row (r = 0)
+    // ---- rank-1 write, requantize, store: FP16 row (r = 0) ----
     {
-#pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) x[0][c] = __builtin_fmaf(kr[0], bdc[c], x[0][c]);
         uint32_t hw[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            hw[c] = f32_to_f16_bits(x[0][2 * c]) | (f32_to_f16_bits(x[0][2 * c + 1]) << 16);
-        uint8_t *hp = unit + HI_OFF + rg * (DV * 2) + cb * 32;
-        st16(hp, U4{hw[0], hw[1], hw[2], hw[3]});
-        st16(hp + 16, U4{hw[4], hw[5], hw[6], hw[7]});
+        for (int c = 0; c < 8; ++c) {
+            const float e0 = __builtin_fmaf(kr[0], bdc[2 * c], x[0][2 * c]);
+            const float e1 = __builtin_fmaf(kr[0], bdc[2 * c + 1], x[0][2 * c + 1]);
+            hw[c] = f32_to_f16_bits(e0) | (f32_to_f16_bits(e1) << 16);
+        }
+        // Each store instruction covers only every other 16 B of the FP16
+        // rows, so these two use the default cache policy and meet in L2;
+        // as non-temporal stores the half-filled lines each reached HBM as
+        // separate writes (+12% write traffic).
+        buf_store16_cached(st, U4{hw[0], hw[1], hw[2], hw[3]}, off_hi, 0);
+        buf_store16_cached(st, U4{hw[4], hw[5], hw[6], hw[7]}, off_hi + 16, 0);
     }
-    // INT8 rows
+    // ---- INT8 rows ----
 #pragma unroll
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
         float amax = 0.f;
@@ -211,21 +213,17 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
         amax = fmaxf(amax, partner_xor1(amax));
         const float s = group_scale(amax);
         const double rinv = scale_reciprocal(s);
-        uint32_t cw[4];
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
-            cw[c4] = pack4_low_bytes(quant_code_bits(x[r][4 * c4], rinv),
-                                     quant_code_bits(x[r][4 * c4 + 1], rinv),
-                                     quant_code_bits(x[r][4 * c4 + 2], rinv),
-                                     quant_code_bits(x[r][4 * c4 + 3], rinv));
-        const int lrow = rg + 16 * (r - 1);
-        st16(unit + LO_OFF + lrow * DV + cb * 16, U4{cw[0], cw[1], cw[2], cw[3]});
-        if ((cb & 1) == 0)
-            *reinterpret_cast<float *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4) = s;
+        U4 cw;
+        cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
+        cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
+        cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
+        cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
+        buf_store16(st, cw, off_lo, LO_OFF + 2048 * (r - 1));
+        if ((cb & 1) == 0) buf_storef(st, s, off_sc + 256 * (r - 1), SC_OFF);
     }
 }
 
-// Launchers (host).
+// Launcher (host): one workgroup per (slot, head) unit.
 hipError_t launch_decode_i8f16(int kind, const PoolView &pool, const int32_t *slots, int n,
                                const float *q, const float *k, const float *v, const float *gate,
                                const float *beta, float *o, hipStream_t stream) {

@@ -49,8 +49,13 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// IEEE binary16 round-to-nearest-even (v_cvt_f16_f32 in the default mode).
+// IEEE binary16 round-to-nearest-even (v_cvt_f16_f32 in the default mode) of
+// an FP32 value.  The empty asm pins x as a rounded FP32 register value:
+// without it the compiler folds a preceding FP32 fma into v_fma_mix*_f16,
+// which rounds the exact product-sum straight to FP16 (one rounding instead
+// of FP32 then FP16) and so changes some results.
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+    asm volatile("" : "+v"(x));
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
@@ -80,28 +85,92 @@ __device__ __forceinline__ double scale_reciprocal(float s) {
     return s == 0.0f ? 0.0 : r;
 }
 
-// Code of x in a group with reciprocal rinv: RN_int(RN32(x / s)), returned
-// in the low byte (two's complement) of the result.  RN32(x * rinv) in FP64
-// equals RN32(x / s) for the same reason as in group_scale (|rinv - 1/s| is
-// far below the 2^-49 margin); adding 1.5 * 2^23 then rounds the FP32
-// quotient to an integer, half to even, and leaves that integer in the low
-// mantissa bits.  |x / s| <= 127 + 2^-16 keeps the result in [-127, 127].
-__device__ __forceinline__ uint32_t quant_code_bits(float x, double rinv) {
-    float qf = (float)((double)x * rinv);
-    float y = qf + 12582912.0f;
-    return __builtin_bit_cast(uint32_t, y);
+// RN32(x / s) for a group with reciprocal rinv.  The FP64 product is within
+// 2^-52 relative of the exact quotient (|rinv - 1/s| is far below that), and a
+// quotient of two FP32 numbers is never within 2^-49 relative of an FP32
+// rounding midpoint, so rounding the product to FP32 gives the correctly
+// rounded quotient (the same argument as in group_scale).
+__device__ __forceinline__ float quant_quotient(float x, double rinv) {
+    return (float)((double)x * rinv);
 }
 
-// Pack the low bytes of four code words into one dword (byte i <- c_i).
-__device__ __forceinline__ uint32_t pack4_low_bytes(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                    uint32_t c3) {
-    uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);
-    uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x04000c0cu);
-    return lo | hi;
+// Codes of four quotients y0..y3 (|y| <= 127 + 2^-16), packed little-endian
+// (byte i <- code of y_i, two's complement).  Adding 1.5 * 2^23 rounds y to
+// an integer, half to even, and leaves that integer in the low mantissa bits;
+// the SDWA form writes the low byte of each sum straight into byte i of the
+// packed word (dst_sel BYTE_i: result bits [7:0] -> destination bits
+// [8i+7:8i]; the first write zeroes the other bytes, the rest preserve them).
+__device__ __forceinline__ uint32_t pack4_codes(float y0, float y1, float y2, float y3) {
+    const float magic = 12582912.0f;
+    uint32_t d;
+    asm(
+        "v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:DWORD"
+        : "=v"(d)
+        : "v"(y0), "v"(magic));
+    asm(
+        "v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD"
+        : "+v"(d)
+        : "v"(y1), "v"(magic));
+    asm(
+        "v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD"
+        : "+v"(d)
+        : "v"(y2), "v"(magic));
+    asm(
+        "v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD"
+        : "+v"(d)
+        : "v"(y3), "v"(magic));
+    return d;
+}
+
+// Packed codes of four values sharing the reciprocal scale rinv.
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, double rinv) {
+    return pack4_codes(quant_quotient(x0, rinv), quant_quotient(x1, rinv),
+                       quant_quotient(x2, rinv), quant_quotient(x3, rinv));
 }
 
 __device__ __forceinline__ float sext_byte_to_f32(uint32_t w, int b) {
     return (float)(int32_t)(int8_t)(w >> (8 * b));
+}
+
+// ---- raw buffer access -------------------------------------------------
+// A buffer resource holds a uniform base address and a byte range in
+// SGPRs; each lane supplies only a 32-bit offset, and accesses outside
+// [0, bytes) read zero and write nothing.  kStream marks data touched once
+// per step (the state, q/k/v/g, o) as non-temporal.
+struct alignas(16) U4 {
+    uint32_t x, y, z, w;
+};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+constexpr int kStream = 2;              // nt cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes,
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ U4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStream);
+    return U4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, U4 d, int voff, int soff) {
+    const u32x4 v = {d.x, d.y, d.z, d.w};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kStream);
+}
+__device__ __forceinline__ void buf_store16_cached(__amdgpu_buffer_rsrc_t r, U4 d, int voff,
+                                                   int soff) {
+    const u32x4 v = {d.x, d.y, d.z, d.w};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream));
+}
+__device__ __forceinline__ void buf_storef(__amdgpu_buffer_rsrc_t r, float d, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, d), r, voff, soff,
+                                          kStream);
 }
 
 }  // namespace qrs

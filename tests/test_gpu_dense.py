@@ -1,7 +1,14 @@
 """Decode on an uncompressed FP32 state pool (compression disabled) against
-the oracle's FP32 recurrence: readout relative error <= 1e-4 per
-(unit, step), the spec bar for FP32-state mode (DAMP arXiv HTML,
-section 3.1, Eq.(1); stored coordinates of the v2 notes, section 2.7)."""
+the oracle (DAMP arXiv HTML, section 3.1, Eq.(1); stored coordinates of the
+v2 notes, section 2.7).
+
+Bar: readout relative error <= 1e-4 per (unit, step), measured against the
+exact recurrence of the same FP32 inputs (the oracle's FP64 twin).  The
+FP32 oracle is not the reference for this bar: its own sequential FP32 sums
+already reach about 1e-4 of the exact result at some steps, so two correct
+FP32 implementations can differ by up to twice the bar.  The GPU's distance
+to the FP32 oracle is reported alongside.
+"""
 import numpy as np
 import pytest
 import torch
@@ -27,27 +34,34 @@ def run_dense(cfg, kind, n_gpu, H, steps, sample, smooth):
     gp = binding.StatePool(binding.FMT_FP32, n_gpu, H, perm, c)
     S0 = inputs.initial_state(cfg, n_gpu, H)
     gp.store(to_dev(slots, torch.int32), to_dev(S0))
+    local = np.arange(len(sample))
     od = oracle.OracleDensePool(len(sample), H, perm, c)
-    od.set_model(np.arange(len(sample)), S0[sample])
+    od.set_model(local, S0[sample])
+    ox = oracle.OracleDensePool(len(sample), H, perm, c, dtype=np.float64)
+    ox.set_model(local, S0[sample].astype(np.float64))
     ds = to_dev(slots, torch.int32)
-    worst = 0.0
+    worst, worst_f32 = 0.0, 0.0
     for t in range(steps):
         d = inputs.step_inputs(cfg, t, n_gpu, H, kind)
         fn = gp.gdn_step if kind == "gdn" else gp.kda_step
         og = fn(ds, to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), to_dev(_gate(d, kind)),
-                to_dev(d["beta"])).cpu().numpy()[sample]
+                to_dev(d["beta"])).cpu().numpy()[sample].astype(np.float64)
         sub = {key: val[sample] for key, val in d.items()}
-        oo = od.decode_step(np.arange(len(sample)), sub["q"], sub["k"], sub["v"],
-                            _gate(sub, kind), sub["beta"], 0 if kind == "gdn" else 1)
-        rel = np.linalg.norm(og - oo, axis=-1) / np.linalg.norm(oo, axis=-1)
+        args = (local, sub["q"], sub["k"], sub["v"], _gate(sub, kind), sub["beta"],
+                0 if kind == "gdn" else 1)
+        oo = od.decode_step(*args).astype(np.float64)
+        ox_o = ox.decode_step(*args)
+        rel = np.linalg.norm(og - ox_o, axis=-1) / np.linalg.norm(ox_o, axis=-1)
+        rel32 = np.linalg.norm(og - oo, axis=-1) / np.linalg.norm(oo, axis=-1)
         worst = max(worst, float(rel.max()))
-        assert rel.max() <= REL_TOL, f"step {t}: readout rel err {rel.max():.3e}"
+        worst_f32 = max(worst_f32, float(rel32.max()))
+        assert rel.max() <= REL_TOL, f"step {t}: readout rel err {rel.max():.3e} vs exact"
     Tg = gp.dequant(to_dev(sample, torch.int32), binding.SPACE_STORED).cpu().numpy()
-    To = od.T.reshape(len(sample), H, DK, DV)
-    relS = np.linalg.norm((Tg - To).reshape(-1, DK * DV), axis=1) / np.linalg.norm(
-        To.reshape(-1, DK * DV), axis=1)
+    Tx = ox.T.reshape(len(sample), H, DK, DV)
+    relS = np.linalg.norm((Tg - Tx).reshape(-1, DK * DV), axis=1) / np.linalg.norm(
+        Tx.reshape(-1, DK * DV), axis=1)
     assert relS.max() <= REL_TOL
-    return worst
+    return dict(worst_vs_exact=worst, worst_vs_fp32_oracle=worst_f32, state_vs_exact=relS.max())
 
 
 def test_cfg0_dense():
