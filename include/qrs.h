@@ -167,6 +167,29 @@ int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float 
                         const float *k, const float *v, const float *g, const float *beta,
                         float *o, hipStream_t stream);
 
+/*
+ * Chunked prefill with GDN gating, writing the compressed state (DAMP arXiv
+ * HTML, Appendix A.5 "Prefill path"; v2 reading notes, section 2.2): for each
+ * of n sequences (slots[b]) x H heads, runs T tokens through the recurrence
+ * of qrs_gdn_decode_step in FP32 one chunk of `chunk` tokens at a time (the
+ * last chunk may be shorter) and writes the chunk-final state into the slot
+ * at every chunk end; the next chunk continues from the stored (requantized)
+ * state.  Outputs come from the FP32 state inside the chunk.
+ *   q, k, v: [n][T][H][128] in model key order, FP32 (in_dtype 0) or bf16
+ *            (in_dtype 1, widened exactly to FP32 on load);
+ *   alpha, beta: FP32 [n][T][H];  o: FP32 [n][T][H][128], model value order;
+ *   chunk: 1..64;  init_from_pool: 1 = start from the slot's stored state,
+ *   0 = start from zero.
+ * All contractions run on FP32 matrix cores.  FP32 pools store the chunk-end
+ * state uncompressed (compression disabled).  Out-of-range slot ids leave
+ * their state untouched and fill their outputs with NaN.  n = 0 or T = 0 is
+ * a no-op.
+ */
+int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int chunk,
+                        int in_dtype, const void *q, const void *k, const void *v,
+                        const float *alpha, const float *beta, float *o, int init_from_pool,
+                        hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char *qrs_status_string(int status);
 

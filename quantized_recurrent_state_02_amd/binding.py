@@ -31,7 +31,7 @@ HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
 EXPORTED = (
     "qrs_state_pool_bytes", "qrs_create_state_pool", "qrs_destroy_state_pool", "qrs_pool_info",
     "qrs_store_state", "qrs_dequant_state", "qrs_gdn_decode_step", "qrs_kda_decode_step",
-    "qrs_status_string",
+    "qrs_chunked_prefill", "qrs_status_string",
 )
 
 _lib = None
@@ -67,6 +67,8 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [p, p, i, p, p, p, p, p, p, p]
         fn.restype = i
+    lib.qrs_chunked_prefill.argtypes = [p, p, i, i, i, i, p, p, p, p, p, p, i, p]
+    lib.qrs_chunked_prefill.restype = i
     lib.qrs_status_string.argtypes = [i]
     lib.qrs_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -180,6 +182,29 @@ class StatePool:
         n = slots.numel()
         return self._step(load().qrs_gdn_decode_step, "qrs_gdn_decode_step", slots, q, k, v,
                           alpha, (n, self.num_heads), beta, out)
+
+    def prefill(self, slots, q, k, v, alpha, beta, chunk=64, init_from_pool=True, out=None):
+        """Chunked prefill (GDN gating): q, k, v [n][T][H][128] float32 or
+        bfloat16 (one dtype), alpha, beta float32 [n][T][H]; returns o float32
+        [n][T][H][128]."""
+        n = slots.numel()
+        if q.dim() != 4:
+            raise QrsError("q must be [n][T][H][128]")
+        T, H = q.shape[1], self.num_heads
+        dt = q.dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise QrsError("q, k, v must be float32 or bfloat16")
+        if out is None:
+            out = torch.empty((n, T, H, DV), dtype=torch.float32, device=self.mem.device)
+        st = load().qrs_chunked_prefill(
+            self.handle, _dev(slots, torch.int32, (n,), "slots"), n, T, int(chunk),
+            0 if dt == torch.float32 else 1,
+            _dev(q, dt, (n, T, H, DK), "q"), _dev(k, dt, (n, T, H, DK), "k"),
+            _dev(v, dt, (n, T, H, DV), "v"), _dev(alpha, torch.float32, (n, T, H), "alpha"),
+            _dev(beta, torch.float32, (n, T, H), "beta"),
+            _dev(out, torch.float32, (n, T, H, DV), "o"), int(bool(init_from_pool)), _stream())
+        _check(st, "qrs_chunked_prefill")
+        return out
 
     def kda_step(self, slots, q, k, v, g, beta, out=None):
         n = slots.numel()

@@ -21,6 +21,10 @@ hipError_t launch_store(int fmt, const PoolView &pool, const int32_t *slots, int
                         int space, hipStream_t stream);
 hipError_t launch_dequant(int fmt, const PoolView &pool, const int32_t *slots, int n, float *S,
                           int space, hipStream_t stream);
+hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, int n, int T,
+                          int chunk, int in_bf16, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, float *o, int init_from_pool,
+                          hipStream_t stream);
 }  // namespace qrs
 
 struct qrs_pool_s {
@@ -228,6 +232,24 @@ int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float 
                         const float *k, const float *v, const float *g, const float *beta,
                         float *o, hipStream_t stream) {
     return decode_common(1, pool, slots, n, q, k, v, g, beta, o, stream);
+}
+
+int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int chunk,
+                        int in_dtype, const void *q, const void *k, const void *v,
+                        const float *alpha, const float *beta, float *o, int init_from_pool,
+                        hipStream_t stream) {
+    if (!pool || n < 0 || T < 0 || chunk < 1 || chunk > 64 || (in_dtype != 0 && in_dtype != 1) ||
+        (init_from_pool != 0 && init_from_pool != 1))
+        return QRS_EINVAL;
+    if (n == 0 || T == 0) return QRS_OK;
+    if (!slots || !q || !k || !v || !alpha || !beta || !o) return QRS_EINVAL;
+    if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu || T > (1 << 24)) return QRS_EINVAL;
+    DeviceGuard g(pool->device);
+    if (!g.ok) return QRS_EDEVICE;
+    return qrs::launch_prefill(pool->fmt, view(pool), slots, n, T, chunk, in_dtype, q, k, v, alpha,
+                               beta, o, init_from_pool, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
 }
 
 const char *qrs_status_string(int status) {

@@ -1,0 +1,475 @@
+// qrs_prefill.hip -- chunked prefill that writes the compressed state, GDN gating.
+//
+// Prefill runs the FP32 recurrence inside each chunk and writes the chunk-final
+// state into the same packed cache the decode kernel uses; the next chunk and
+// later decode steps read that compressed state (DAMP arXiv HTML, Appendix A.5
+// "Prefill path"; v2 reading notes, section 2.2).  The pages give no chunk
+// algebra, so the one used here is derived from the delta form of the update
+// (HTML section 3.1, Eq.(1)) in stored coordinates (v2 notes, section 2.7).
+//
+// Within a chunk of C tokens starting from state S0 (GDN: Lambda_t = alpha_t I),
+// let g_t = alpha_1 ... alpha_t (g_0 = 1) and r(t, i) = g_t / g_i.  With
+// delta_t = beta_t (v'_t - alpha_t S_{t-1}^T k'_t) the update is
+// S_t = alpha_t S_{t-1} + k'_t delta_t^T, so
+//     S_t     = g_t S0 + sum_{i<=t} r(t, i) k'_i delta_i^T
+//     delta_t = beta_t (v'_t - g_t S0^T k'_t - sum_{i<t} r(t, i) (k'_i . k'_t) delta_i).
+// In matrix form over the chunk (rows = tokens), with M[t][i] = r(t,i) k'_t.k'_i
+// for i < t:
+//     (I + B M) [W | U] = B [Gamma K | V]        (unit lower triangular)
+//     Delta = U - W S0
+//     O     = Gamma Q S0 + (L o Q K^T) Delta,     L[t][i] = r(t, i) for i <= t
+//     S_C   = g_C S0 + K^T diag(r(C, t)) Delta.
+// Decay ratios are taken from FP64 prefix sums of log(alpha) (a chunk product
+// of alphas underflows FP32); a zero alpha makes every ratio across it zero.
+//
+// Launch: one 256-thread workgroup (four wave64) per (sequence, head); chunks
+// run in order.  Per chunk the waves share K, Q, V/U, W and the two 64x64
+// masked Gram tiles in LDS; wave w owns value columns [32w, 32w + 32) of S0,
+// Delta and O, which stay in registers in the accumulator layout of
+// v_mfma_f32_16x16x4f32 (lane l holds column l & 15 of rows 4 (l >> 4) + r of
+// each 16x16 tile).  That layout feeds the next contraction's B operand
+// directly when the contraction index inside each 16-block is taken in the
+// order 4 (l >> 4) + j at step j.  Every contraction runs on FP32 MFMA; the
+// unit lower triangular solve goes block by block (16 tokens): a
+// column-parallel substitution on the VALU inside each diagonal block and
+// MFMA updates of the later blocks.  At
+// each chunk end the state is requantized through an LDS copy of the packed
+// unit, stored with 16-byte writes, and dequantized back into registers (the
+// same values a reload of the stored unit gives).
+#include "qrs_internal.h"
+
+namespace qrs {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int PT = 256;     // threads per workgroup
+constexpr int CT = 64;      // tokens per tile (chunks <= 64 are zero-padded)
+constexpr int LDK = 132;    // row stride (floats) of the [64][128] LDS tiles
+constexpr int LDM = 68;     // row stride of the [64][64] Gram tile
+
+struct PrefillSmem {
+    float K[CT * LDK];   // k' (stored key order)
+    float Q[CT * LDK];   // q'; at chunk end, the packed unit being written
+    float VU[CT * LDK];  // v' = v / c, then U = T V in place
+    float W[CT * LDK];   // W = T Gamma K
+    float M[CT * LDM];   // strict-lower decayed K K^T, then inclusive-lower decayed Q K^T
+    double lg[CT];       // prefix sum of log(alpha) over the non-zero alphas
+    int zi[CT];          // last token <= t with alpha = 0 (-1 if none)
+    float gam[CT];       // g_t
+    float rc[CT];        // r(C, t): decay from token t to the chunk end
+    float bet[CT];
+};
+static_assert(sizeof(PrefillSmem) <= 160 * 1024, "fits the 160 KB LDS of a gfx950 CU");
+
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f lds4(const float *p) { return *reinterpret_cast<const v4f *>(p); }
+
+// r(t, i) = prod_{j=i+1..t} alpha_j for i < t inside the tile.
+__device__ __forceinline__ float ratio(const PrefillSmem &s, int t, int i) {
+    if (s.zi[t] > i) return 0.f;
+    return expf((float)(s.lg[t] - s.lg[i]));
+}
+
+template <int IN_BF16>
+__device__ __forceinline__ float ld_in(const void *p, size_t idx) {
+    if (IN_BF16) {
+        const uint16_t bits = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p) + idx);
+        return __builtin_bit_cast(float, (uint32_t)bits << 16);
+    }
+    return __builtin_nontemporal_load(reinterpret_cast<const float *>(p) + idx);
+}
+
+// 16x16 tile of the masked Gram matrix  A[t][i] = r(t, i) * (X_t . K_i)  for
+// i < t (STRICT) or i <= t, zero elsewhere, rows t in [16 tb, +16), columns i
+// in [16 sb, +16); X = K or Q from LDS.  Written to s.M.
+template <bool STRICT>
+__device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, int tb, int sb, int l16,
+                                          int g) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const v4f a = lds4(X + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
+        const v4f b = lds4(s.K + (16 * sb + l16) * LDK + 16 * kb + 4 * g);
+        acc = mfma4(a.x, b.x, acc);
+        acc = mfma4(a.y, b.y, acc);
+        acc = mfma4(a.z, b.z, acc);
+        acc = mfma4(a.w, b.w, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g + r, i = 16 * sb + l16;
+        const bool keep = STRICT ? (i < t) : (i <= t);
+        s.M[t * LDM + i] = keep ? ratio(s, t, i) * acc[r] : 0.f;
+    }
+}
+
+}  // namespace
+
+// FMT: QRS_FMT_I8F16 (1) or QRS_FMT_FP32 (0) pool; IN_BF16: q, k, v in bf16.
+template <int FMT, int IN_BF16>
+__global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_t *__restrict__ slots,
+                                                     int T, int chunk, const void *__restrict__ q,
+                                                     const void *__restrict__ k,
+                                                     const void *__restrict__ v,
+                                                     const float *__restrict__ alpha,
+                                                     const float *__restrict__ beta,
+                                                     float *__restrict__ o, int init_from_pool) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    PrefillSmem &s = *reinterpret_cast<PrefillSmem *>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;  // wave: value columns [32 w, 32 w + 32)
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
+    const int H = pool.num_heads;
+    const int uu = blockIdx.x;  // b * H + h
+    const int b = uu / H;
+    const int h = uu - b * H;
+    const int slot = slots[b];
+    const size_t unit_bytes = FMT == 1 ? (size_t)UNIT_BYTES : (size_t)F32_UNIT_BYTES;
+
+    if (slot < 0 || slot >= pool.num_slots) {
+        for (int e = tid; e < T * DV; e += PT) {
+            const int t = e >> 7, j = e & (DV - 1);
+            o[(((size_t)b * T + t) * H + h) * DV + j] = __builtin_nanf("");
+        }
+        return;
+    }
+    uint8_t *unit = pool.base + ((size_t)slot * H + h) * unit_bytes;
+    const int in_col = tid & (DK - 1);                      // column this thread loads
+    const int perm_col = pool.perm[h * DK + in_col];        // model key channel of stored row in_col
+    const float c_in = pool.smooth[h * DV + in_col];
+    float c_out[2];
+    c_out[0] = pool.smooth[h * DV + 32 * w + l16];
+    c_out[1] = pool.smooth[h * DV + 32 * w + 16 + l16];
+
+    // ---- initial state, in the accumulator layout: S[rb][cb][r] holds row
+    //      16 rb + 4 g + r, column 32 w + 16 cb + l16 ----
+    v4f S[8][2];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) S[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (init_from_pool) {
+        if (FMT == 1) {
+            uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
+            for (int e = tid; e < UNIT_BYTES / 16; e += PT)
+                reinterpret_cast<U4 *>(stg)[e] = reinterpret_cast<const U4 *>(unit)[e];
+            __syncthreads();
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * rb + 4 * g + r, col = 32 * w + 16 * cb + l16;
+                        if (rb == 0) {
+                            S[rb][cb][r] = f16_bits_to_f32(
+                                reinterpret_cast<const uint16_t *>(stg + HI_OFF)[row * DV + col]);
+                        } else {
+                            const int lr = row - KHI;
+                            const float sc = reinterpret_cast<const float *>(stg + SC_OFF)[lr * NGRP + w];
+                            S[rb][cb][r] =
+                                sc * (float)reinterpret_cast<const int8_t *>(stg + LO_OFF)[lr * DV + col];
+                        }
+                    }
+            __syncthreads();
+        } else {
+            const float *u = reinterpret_cast<const float *>(unit);
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S[rb][cb][r] = u[(16 * rb + 4 * g + r) * DV + 32 * w + 16 * cb + l16];
+        }
+    }
+
+    const int nchunks = (T + chunk - 1) / chunk;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int t0 = ch * chunk;
+        const int ceff = min(chunk, T - t0);
+
+        // ---- 1. chunk operands into LDS (tokens >= ceff are zero, alpha 1) ----
+        for (int e = tid; e < CT * DK; e += PT) {
+            const int t = e >> 7;
+            float kv = 0.f, qv = 0.f, vv = 0.f;
+            if (t < ceff) {
+                const size_t base = (((size_t)b * T + (t0 + t)) * H + h) * DK;
+                kv = ld_in<IN_BF16>(k, base + perm_col);
+                qv = ld_in<IN_BF16>(q, base + perm_col);
+                vv = ld_in<IN_BF16>(v, base + in_col) / c_in;  // v' = D_c^{-1} v
+            }
+            s.K[t * LDK + in_col] = kv;
+            s.Q[t * LDK + in_col] = qv;
+            s.VU[t * LDK + in_col] = vv;
+        }
+        // ---- 2. decay prefix sums (wave 0: lane = token) ----
+        if (tid < CT) {
+            const int t = tid;
+            const size_t gi = ((size_t)b * T + (t0 + t)) * H + h;
+            const float a = t < ceff ? alpha[gi] : 1.f;
+            double la = a > 0.f ? log((double)a) : 0.0;
+            int z = a > 0.f ? -1 : t;
+#pragma unroll
+            for (int off = 1; off < CT; off <<= 1) {
+                const double lo = __shfl_up(la, off, 64);
+                const int zo = __shfl_up(z, off, 64);
+                if (lane >= off) {
+                    la += lo;
+                    z = max(z, zo);
+                }
+            }
+            s.lg[t] = la;
+            s.zi[t] = z;
+            s.gam[t] = z >= 0 ? 0.f : expf((float)la);
+            s.bet[t] = t < ceff ? beta[gi] : 0.f;
+        }
+        __syncthreads();
+        if (tid < CT) {
+            const int t = tid;
+            s.rc[t] = t == CT - 1 ? 1.f : ratio(s, CT - 1, t);
+        }
+
+        // ---- 3. M = strict-lower decayed K K^T (10 lower tiles over 4 waves) ----
+        for (int tile = w; tile < 10; tile += 4) {
+            const int tb = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
+            const int sb = tile - tb * (tb + 1) / 2;
+            gram_tile<true>(s, s.K, tb, sb, l16, g);
+        }
+        __syncthreads();
+
+        // ---- 4. (I + B M) X = B R, in place on R = [Gamma K | V] held in
+        //      [W | VU], one 16-token block at a time: a column-parallel
+        //      substitution inside the diagonal block, then MFMA updates of the
+        //      later blocks' right-hand sides ----
+        for (int e = tid; e < CT * DK; e += PT) {
+            const int t = e >> 7;
+            s.W[t * LDK + in_col] = s.gam[t] * s.K[t * LDK + in_col];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            {
+                float *X = tid < DK ? s.W : s.VU;
+                float x[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const int row = 16 * bb + t;
+                    float acc = X[row * LDK + in_col];
+                    const float *mrow = s.M + row * LDM + 16 * bb;
+#pragma unroll
+                    for (int i = 0; i < t; ++i) acc = __builtin_fmaf(-mrow[i], x[i], acc);
+                    x[t] = s.bet[row] * acc;
+                    X[row * LDK + in_col] = x[t];
+                }
+            }
+            __syncthreads();
+            if (bb < 3) {
+                // wave w updates 64 of the 256 right-hand-side columns
+                float *X = w < 2 ? s.W : s.VU;
+#pragma unroll
+                for (int b2 = bb + 1; b2 < 4; ++b2) {
+                    const v4f a = lds4(s.M + (16 * b2 + l16) * LDM + 16 * bb + 4 * g);
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                        const int col = 64 * (w & 1) + 16 * ct + l16;
+                        v4f acc = {0.f, 0.f, 0.f, 0.f};
+                        acc = mfma4(a.x, X[(16 * bb + 4 * g + 0) * LDK + col], acc);
+                        acc = mfma4(a.y, X[(16 * bb + 4 * g + 1) * LDK + col], acc);
+                        acc = mfma4(a.z, X[(16 * bb + 4 * g + 2) * LDK + col], acc);
+                        acc = mfma4(a.w, X[(16 * bb + 4 * g + 3) * LDK + col], acc);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) X[(16 * b2 + 4 * g + r) * LDK + col] -= acc[r];
+                    }
+                }
+                __syncthreads();
+            }
+        }
+
+        // ---- 5. A_qk = inclusive-lower decayed Q K^T (reuses s.M) ----
+        for (int tile = w; tile < 10; tile += 4) {
+            const int tb = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
+            const int sb = tile - tb * (tb + 1) / 2;
+            gram_tile<false>(s, s.Q, tb, sb, l16, g);
+        }
+        __syncthreads();
+
+        // ---- 6. per wave: Delta = U - W S0 ----
+        v4f D[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    const v4f a = lds4(s.W + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
+                    acc = mfma4(a.x, S[kb][cb][0], acc);
+                    acc = mfma4(a.y, S[kb][cb][1], acc);
+                    acc = mfma4(a.z, S[kb][cb][2], acc);
+                    acc = mfma4(a.w, S[kb][cb][3], acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    D[tb][cb][r] =
+                        s.VU[(16 * tb + 4 * g + r) * LDK + 32 * w + 16 * cb + l16] - acc[r];
+            }
+
+        // ---- 7. O = Gamma Q S0 + A_qk Delta, written as o = c (.) O ----
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    const v4f a = lds4(s.Q + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
+                    acc = mfma4(a.x, S[kb][cb][0], acc);
+                    acc = mfma4(a.y, S[kb][cb][1], acc);
+                    acc = mfma4(a.z, S[kb][cb][2], acc);
+                    acc = mfma4(a.w, S[kb][cb][3], acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] *= s.gam[16 * tb + 4 * g + r];
+#pragma unroll
+                for (int sb = 0; sb <= tb; ++sb) {
+                    const v4f a = lds4(s.M + (16 * tb + l16) * LDM + 16 * sb + 4 * g);
+                    acc = mfma4(a.x, D[sb][cb][0], acc);
+                    acc = mfma4(a.y, D[sb][cb][1], acc);
+                    acc = mfma4(a.z, D[sb][cb][2], acc);
+                    acc = mfma4(a.w, D[sb][cb][3], acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tb + 4 * g + r;
+                    if (t < ceff)
+                        __builtin_nontemporal_store(
+                            c_out[cb] * acc[r],
+                            o + (((size_t)b * T + (t0 + t)) * H + h) * DV + 32 * w + 16 * cb + l16);
+                }
+            }
+
+        // ---- 8. S_C = g_C S0 + K^T diag(r(C, t)) Delta ----
+        {
+            const float gc = s.gam[CT - 1];
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) S[rb][cb] *= gc;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float f = s.rc[16 * tb + 4 * g + r];
+                    D[tb][0][r] *= f;
+                    D[tb][1][r] *= f;
+                }
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    float a[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        a[j] = s.K[(16 * kb + 4 * g + j) * LDK + 16 * rb + l16];
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        S[rb][cb] = mfma4(a[0], D[kb][cb][0], S[rb][cb]);
+                        S[rb][cb] = mfma4(a[1], D[kb][cb][1], S[rb][cb]);
+                        S[rb][cb] = mfma4(a[2], D[kb][cb][2], S[rb][cb]);
+                        S[rb][cb] = mfma4(a[3], D[kb][cb][3], S[rb][cb]);
+                    }
+                }
+        }
+        __syncthreads();  // every wave is done with s.Q and s.K
+
+        // ---- 9. chunk end: store the state, continue from what was stored ----
+        if (FMT == 1) {
+            uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rb + 4 * g + r;
+                    float v0 = S[rb][0][r], v1 = S[rb][1][r];
+                    const int c0 = 32 * w + l16, c1 = c0 + 16;
+                    if (rb == 0) {
+                        const uint32_t h0 = f32_to_f16_bits(v0), h1 = f32_to_f16_bits(v1);
+                        uint16_t *hp = reinterpret_cast<uint16_t *>(stg + HI_OFF);
+                        hp[row * DV + c0] = (uint16_t)h0;
+                        hp[row * DV + c1] = (uint16_t)h1;
+                        S[rb][0][r] = f16_bits_to_f32(h0);
+                        S[rb][1][r] = f16_bits_to_f32(h1);
+                    } else {
+                        // this wave's 32 columns are exactly one 32-value group
+                        float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+                        for (int off = 1; off < 16; off <<= 1)
+                            amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+                        const float sc = group_scale(amax);
+                        const double rinv = scale_reciprocal(sc);
+                        const float q0 = rintf(quant_quotient(v0, rinv));
+                        const float q1 = rintf(quant_quotient(v1, rinv));
+                        const int lr = row - KHI;
+                        int8_t *cp = reinterpret_cast<int8_t *>(stg + LO_OFF);
+                        cp[lr * DV + c0] = (int8_t)(int)q0;
+                        cp[lr * DV + c1] = (int8_t)(int)q1;
+                        if (l16 == 0) reinterpret_cast<float *>(stg + SC_OFF)[lr * NGRP + w] = sc;
+                        S[rb][0][r] = sc * q0;
+                        S[rb][1][r] = sc * q1;
+                    }
+                }
+            __syncthreads();
+            for (int e = tid; e < UNIT_BYTES / 16; e += PT)
+                reinterpret_cast<U4 *>(unit)[e] = reinterpret_cast<const U4 *>(stg)[e];
+        } else {
+            float *u = reinterpret_cast<float *>(unit);
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        u[(16 * rb + 4 * g + r) * DV + 32 * w + 16 * cb + l16] = S[rb][cb][r];
+        }
+        __syncthreads();  // the staging copy is read out before the next chunk's loads
+    }
+}
+
+hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, int n, int T,
+                          int chunk, int in_bf16, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, float *o, int init_from_pool,
+                          hipStream_t stream) {
+    const size_t smem = sizeof(PrefillSmem);
+    dim3 grid((unsigned)(n * pool.num_heads)), block(PT);
+#define QRS_PREFILL_CASE(F, B)                                                                    \
+    if (fmt == F && in_bf16 == B) {                                                               \
+        static bool attr_set = false;                                                             \
+        if (!attr_set) {                                                                          \
+            hipError_t e = hipFuncSetAttribute(                                                   \
+                reinterpret_cast<const void *>(&prefill_kernel<F, B>),                            \
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);                           \
+            if (e != hipSuccess) return e;                                                        \
+            attr_set = true;                                                                      \
+        }                                                                                         \
+        hipLaunchKernelGGL((prefill_kernel<F, B>), grid, block, smem, stream, pool, slots, T,     \
+                           chunk, q, k, v, alpha, beta, o, init_from_pool);                       \
+        return hipGetLastError();                                                                 \
+    }
+    QRS_PREFILL_CASE(1, 0)
+    QRS_PREFILL_CASE(1, 1)
+    QRS_PREFILL_CASE(0, 0)
+    QRS_PREFILL_CASE(0, 1)
+#undef QRS_PREFILL_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qrs

@@ -98,3 +98,14 @@ def test_split_units_layout():
     raw[0, 2:4] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
     hi, lo, sc = binding.split_units(raw)
     assert lo[1, 5, 3] == -2 and sc[1, 0, 0] == 0.5 and hi[0, 0, 1] == 0x3C00
+
+
+def test_prefill_argument_validation(lib):
+    f = lib.qrs_chunked_prefill
+    p = ctypes.c_void_p(0x10000)
+    assert f(None, p, 1, 8, 64, 0, p, p, p, p, p, p, 1, None) == -1      # null pool
+    # bad sizes and enums are rejected before the pool is touched
+    fake = ctypes.c_void_p(0x20000)
+    for n, T, chunk, dt, init in ((-1, 8, 64, 0, 1), (1, -1, 64, 0, 1), (1, 8, 0, 0, 1),
+                                  (1, 8, 65, 0, 1), (1, 8, 64, 2, 1), (1, 8, 64, 0, 2)):
+        assert f(fake, p, n, T, chunk, dt, p, p, p, p, p, p, init, None) == -1

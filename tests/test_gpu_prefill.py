@@ -1,0 +1,262 @@
+"""Chunked prefill (GDN gating) writing the compressed state, on the GPU
+against the oracle (DAMP arXiv HTML, Appendix A.5 "Prefill path"; v2 reading
+notes, section 2.2: FP32 recurrence inside a chunk, the chunk-final state
+written to the packed cache and read back by the next chunk).
+
+The checks are layered:
+
+* Compression disabled (FP32 pool): the GPU's chunked algebra against the
+  exact recurrence of the same FP32 inputs (the oracle's FP64 twin, token by
+  token): readout and final state relative error <= 1e-4.
+* Compressed pool, one chunk at a time from identical starts: before every
+  chunk the GPU's stored bytes are copied into the oracle's pool, so both
+  start from the same packed state.  Outputs are checked against the exact
+  recurrence from that state: relative error <= 1e-4 per (unit, token), or,
+  on the rare ill-conditioned tokens where the method's own sequential FP32
+  evaluation (the oracle) already misses 1e-4 (a readout norm far below its
+  terms, e.g. 8e-5 against O(0.1) on config 3), no more than four times the
+  oracle's error on that token.  The requantized
+  chunk-end state against the oracle's (sequential FP32, then quantized):
+  INT8 codes at most one step apart (scale difference and the FP32 rounding of
+  s * code allowed), FP16 rows within one FP16 ulp plus FP32 cancellation
+  noise (2^-20 of the row's largest magnitude).
+* One call over all T tokens equals the same tokens sent one chunk per call,
+  bit for bit (outputs and every stored byte), so the full-size launch
+  inherits the per-chunk checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_recurrent_state_02_amd import binding, inputs
+from tests.parity_util import dequant_units, oracle_units, split_gpu, to_dev, ulp16
+
+pytestmark = pytest.mark.gpu
+DK = DV = 128
+REL_TOL = 1e-4
+
+
+def _exact_chunk(T0, perm, c, d, t0, t1):
+    """FP64 recurrence (stored coordinates) of tokens [t0, t1) from the
+    stored-space states T0 [n*H][128][128]; returns (outputs [n][t][H][128],
+    final states)."""
+    n, H = d["q"].shape[0], d["q"].shape[2]
+    ox = oracle.OracleDensePool(n, H, perm, c, dtype=np.float64)
+    ox.T[:] = T0.reshape(n * H, DK, DV)
+    outs = []
+    for t in range(t0, t1):
+        outs.append(ox.decode_step(np.arange(n), d["q"][:, t], d["k"][:, t], d["v"][:, t],
+                                   d["alpha"][:, t], d["beta"][:, t], 0))
+    return np.stack(outs, axis=1), ox.T.copy()
+
+
+def _rel_rows(a, b):
+    """Relative 2-norm error over the last axis."""
+    a = a.astype(np.float64)
+    b = b.astype(np.float64)
+    return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-300)
+
+
+def _dev_inputs(d, bf16):
+    dt = torch.bfloat16 if bf16 else torch.float32
+    out = {key: to_dev(d[key]).to(dt) for key in ("q", "k", "v")}
+    out["alpha"] = to_dev(d["alpha"])
+    out["beta"] = to_dev(d["beta"])
+    return out
+
+
+def _as_seen(d, dev):
+    """The FP32 values the GPU consumes (bf16 inputs widened exactly)."""
+    e = dict(d)
+    for key in ("q", "k", "v"):
+        e[key] = dev[key].float().cpu().numpy()
+    return e
+
+
+# ---------------------------------------------------------------------------
+# compression disabled
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,chunk,bf16,init", [
+    (200, 64, False, False),   # 3 full chunks and a ragged tail
+    (200, 64, False, True),    # from a stored initial state
+    (96, 16, False, True),
+    (13, 1, False, True),      # chunk 1: a sequence of single-token updates
+    (130, 64, True, True),     # bf16 inputs
+])
+def test_prefill_fp32_pool_matches_exact(T, chunk, bf16, init):
+    n, H, cfg = 2, 4, 3
+    perm = inputs.protected_perm(31, H)
+    c = inputs.smoothing(31, H, True)
+    d = inputs.prefill_inputs(cfg, n, H, T)
+    dev = _dev_inputs(d, bf16)
+    d = _as_seen(d, dev)
+    slots = np.array([1, 0], np.int32)
+    gp = binding.StatePool(binding.FMT_FP32, 2, H, perm, c)
+    S0 = inputs.initial_state(31, n, H) if init else np.zeros((n, H, DK, DV), np.float32)
+    gp.store(to_dev(slots, torch.int32), to_dev(S0))
+    T0 = gp.dequant(to_dev(slots, torch.int32), binding.SPACE_STORED).cpu().numpy()
+    o = gp.prefill(to_dev(slots, torch.int32), dev["q"], dev["k"], dev["v"], dev["alpha"],
+                   dev["beta"], chunk=chunk, init_from_pool=init).cpu().numpy()
+    ox, Tx = _exact_chunk(T0.astype(np.float64), perm, c, d, 0, T)
+    rel = _rel_rows(o, ox)
+    assert rel.max() <= REL_TOL, f"readout rel err {rel.max():.3e} at {np.unravel_index(rel.argmax(), rel.shape)}"
+    Tg = gp.dequant(to_dev(slots, torch.int32), binding.SPACE_STORED).cpu().numpy()
+    relS = np.linalg.norm((Tg.reshape(n * H, -1) - Tx.reshape(n * H, -1)), axis=1) / \
+        np.linalg.norm(Tx.reshape(n * H, -1), axis=1)
+    assert relS.max() <= REL_TOL, f"state rel err {relS.max():.3e}"
+
+
+# ---------------------------------------------------------------------------
+# compressed pool
+# ---------------------------------------------------------------------------
+
+def _load_units_into_oracle(op, gp, slots):
+    hi, lo, sc = split_gpu(gp, slots)
+    H = op.num_heads
+    idx = (np.asarray(slots)[:, None] * H + np.arange(H)[None, :]).ravel()
+    op.hi[idx], op.lo[idx], op.sc[idx] = hi, lo, sc
+
+
+def _check_chunk_end(gu, ou):
+    """Requantized chunk-end states: INT8 codes at most one step apart, FP16
+    rows within one ulp plus FP32 cancellation noise."""
+    Tg = dequant_units(*gu).astype(np.float64)
+    To = dequant_units(*ou).astype(np.float64)
+    sg, so = gu[2].astype(np.float64), ou[2].astype(np.float64)
+    d = np.abs(Tg - To)
+    step = np.repeat(np.maximum(sg, so) + 127.0 * np.abs(sg - so), 32, axis=-1)
+    rnd = 0.5 * (np.spacing(np.abs(Tg[:, 16:]).astype(np.float32))
+                 + np.spacing(np.abs(To[:, 16:]).astype(np.float32)))
+    assert np.all(d[:, 16:] <= step + rnd), f"INT8 rows beyond one step: {(d[:, 16:] > step + rnd).sum()}"
+    row_max = np.maximum(np.abs(Tg[:, :16]), np.abs(To[:, :16])).max(axis=-1, keepdims=True)
+    lim = ulp16(np.maximum(np.abs(Tg[:, :16]), np.abs(To[:, :16]))) + 2.0 ** -20 * row_max
+    assert np.all(d[:, :16] <= lim), f"FP16 rows beyond one ulp: {(d[:, :16] > lim).sum()}"
+    return int((gu[1] != ou[1]).sum())
+
+
+def run_chunkwise(n, H, T, chunk, bf16, perm, c, slots, S0, d, dev, sample):
+    """Send the tokens one chunk per call; before each chunk copy the GPU's
+    stored units of the sampled slots into the oracle and check that chunk.
+    Returns (GPU pool, outputs, worst relative readout error, code flips)."""
+    gp = binding.StatePool(binding.FMT_I8F16, int(slots.max()) + 1, H, perm, c)
+    ds = to_dev(slots, torch.int32)
+    if S0 is not None:
+        gp.store(ds, to_dev(S0))
+    op = oracle.OraclePool(int(slots.max()) + 1, H, perm, c)
+    o_all = torch.empty((n, T, H, DV), device="cuda")
+    samp = np.asarray(sample)
+    ds_ = {key: val[samp] for key, val in d.items()}
+    worst, flips = 0.0, 0
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        sub = {key: val[:, t0:t1].contiguous() for key, val in dev.items()}
+        init = S0 is not None or t0 > 0
+        _load_units_into_oracle(op, gp, slots[samp])
+        T0 = op.dequant(slots[samp], binding.SPACE_STORED) if init else \
+            np.zeros((len(samp), H, DK, DV), np.float32)
+        og = gp.prefill(ds, sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], chunk=chunk,
+                        init_from_pool=init)
+        o_all[:, t0:t1] = og
+        oo = op.prefill(slots[samp], ds_["q"][:, t0:t1], ds_["k"][:, t0:t1], ds_["v"][:, t0:t1],
+                        ds_["alpha"][:, t0:t1], ds_["beta"][:, t0:t1], chunk, init)
+        ox, _ = _exact_chunk(T0.astype(np.float64), perm, c, ds_, t0, t1)
+        og_s = og.cpu().numpy()[samp]
+        rel = _rel_rows(og_s, ox)
+        rel_orc = _rel_rows(oo, ox)          # the sequential FP32 evaluation's own error
+        worst = max(worst, float(rel.max()))
+        lim = np.maximum(REL_TOL, 4.0 * rel_orc)
+        bad = rel > lim
+        assert not bad.any(), (f"chunk at {t0}: readout rel err {rel[bad].max():.3e} vs exact "
+                               f"(sequential FP32: {rel_orc[bad].max():.3e})")
+        flips += _check_chunk_end(split_gpu(gp, slots[samp]), oracle_units(op, slots[samp]))
+        del oo
+    return gp, o_all, worst, flips
+
+
+@pytest.mark.parametrize("T,chunk,bf16,init", [
+    (200, 64, False, True),
+    (200, 64, False, False),
+    (72, 16, True, True),
+])
+def test_prefill_compressed_chunkwise_vs_oracle(T, chunk, bf16, init):
+    n, H, cfg = 3, 4, 3
+    perm = inputs.protected_perm(32, H)
+    c = inputs.smoothing(32, H, True)
+    d = inputs.prefill_inputs(cfg, n, H, T)
+    dev = _dev_inputs(d, bf16)
+    d = _as_seen(d, dev)
+    slots = np.array([4, 0, 2], np.int32)
+    S0 = inputs.initial_state(32, n, H) if init else None
+    _, _, worst, flips = run_chunkwise(n, H, T, chunk, bf16, perm, c, slots, S0, d, dev,
+                                       sample=[0, 1, 2])
+    print(dict(worst_readout_rel=worst, int8_code_flips=flips))
+
+
+def test_single_call_equals_chunkwise_calls():
+    n, H, T, chunk = 2, 4, 200, 64
+    perm = inputs.protected_perm(33, H)
+    c = inputs.smoothing(33, H, True)
+    d = inputs.prefill_inputs(3, n, H, T)
+    dev = _dev_inputs(d, False)
+    slots = np.array([1, 0], np.int32)
+    S0 = inputs.initial_state(33, n, H)
+    ds = to_dev(slots, torch.int32)
+    g1 = binding.StatePool(binding.FMT_I8F16, 2, H, perm, c)
+    g1.store(ds, to_dev(S0))
+    o1 = g1.prefill(ds, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], chunk=chunk)
+    g2 = binding.StatePool(binding.FMT_I8F16, 2, H, perm, c)
+    g2.store(ds, to_dev(S0))
+    o2 = torch.empty_like(o1)
+    for t0 in range(0, T, chunk):
+        sub = {key: val[:, t0:t0 + chunk].contiguous() for key, val in dev.items()}
+        o2[:, t0:t0 + chunk] = g2.prefill(ds, sub["q"], sub["k"], sub["v"], sub["alpha"],
+                                          sub["beta"], chunk=chunk)
+    assert torch.equal(o1, o2)
+    assert torch.equal(g1.units(), g2.units())
+
+
+def test_prefill_invalid_slot_and_empty():
+    H = 2
+    gp = binding.StatePool(binding.FMT_I8F16, 2, H)
+    S0 = np.random.default_rng(5).normal(size=(2, H, DK, DV)).astype(np.float32)
+    gp.store(to_dev(np.arange(2, dtype=np.int32), torch.int32), to_dev(S0))
+    before = gp.units().clone()
+    d = inputs.prefill_inputs(3, 2, H, 10)
+    dev = _dev_inputs(d, False)
+    o = gp.prefill(to_dev(np.array([1, 7], np.int32), torch.int32), dev["q"], dev["k"], dev["v"],
+                   dev["alpha"], dev["beta"], chunk=4).cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[0]))
+    per_slot = (gp.units() != before).view(2, H, -1).any(dim=-1).any(dim=-1).cpu().numpy()
+    assert per_slot.tolist() == [False, True]
+    z = torch.empty((2, 0, H, DK), device="cuda")
+    zg = torch.empty((2, 0, H), device="cuda")
+    after = gp.units().clone()
+    gp.prefill(to_dev(np.arange(2, dtype=np.int32), torch.int32), z, z, z, zg, zg)
+    assert torch.equal(gp.units(), after)
+
+
+def test_full_prefill_shape():
+    """8 sequences x 32 heads x 4,096 tokens in chunks of 64, the benchmarked
+    launch (one call), equals the chunk-per-call run bit for bit; that run is
+    checked against the oracle chunk by chunk on a seeded sample of units."""
+    wl = inputs.WORKLOADS[3]
+    n, H, T, chunk = wl.n, wl.heads, wl.steps, wl.chunk
+    perm = inputs.protected_perm(3, H)
+    c = inputs.smoothing(3, H, False)
+    d = inputs.prefill_inputs(3, n, H, T)
+    dev = _dev_inputs(d, False)
+    slots = np.arange(n, dtype=np.int32)
+    ds = to_dev(slots, torch.int32)
+    g1 = binding.StatePool(binding.FMT_I8F16, n, H, perm, c)
+    o1 = g1.prefill(ds, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], chunk=chunk,
+                    init_from_pool=False)
+    torch.cuda.synchronize()
+    # oracle sample: 2 sequences (all 32 heads) checked at every chunk end
+    sample = np.sort(np.random.default_rng(3).choice(n, 2, replace=False))
+    g2, o2, worst, flips = run_chunkwise(n, H, T, chunk, False, perm, c, slots, None, d, dev,
+                                         sample)
+    assert torch.equal(o1, o2), "single call differs from chunk-per-call run"
+    assert torch.equal(g1.units(), g2.units())
+    print(dict(worst_readout_rel=worst, int8_code_flips=flips))
