@@ -23,6 +23,11 @@ single-pool figure is reported beside it.
 The CPU baseline is the oracle (oracle/, FP32 C code with OpenMP over units)
 timed on a bounded sample of the same workload.
 
+`detail` also reports KDA decode, the single-pool variants, the FP32-state
+kernel on the same inputs, and the chunked prefill kernel (8 x 32 heads x
+4096 tokens, chunks of 64, FP32 and bf16 q/k/v) against the FP32 matrix-core
+peak.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 from __future__ import annotations
@@ -131,6 +136,64 @@ def run_decode(torch, binding, inputs, kind, fmt, dev_in, perm, c, n, H, steps, 
     return secs, ok
 
 
+# Chunked prefill (FP32 matrix cores): algorithmic FLOP per (chunk, head) of
+# the chunk form, C = 64 tokens, d = 128: the two masked Gram products and the
+# triangular solve (5 C^2 d) plus W S0, Q S0 and K^T Delta (6 C d^2).
+PREFILL_CHUNK = 64
+PREFILL_FLOP_PER_CHUNK_HEAD = 5 * 64 * 64 * 128 + 6 * 64 * 128 * 128
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def run_prefill(torch, binding, inputs, bf16, reps=3):
+    """Prefill workload: 8 sequences x 32 heads x 4096 tokens in chunks of 64,
+    GDN gating, fresh requests (zero initial state), compressed pool.  Returns
+    (seconds per call, stats dict)."""
+    wl = inputs.WORKLOADS[3]
+    n, H, T = wl.n, wl.heads, wl.steps
+    t0 = time.time()
+    d = inputs.prefill_inputs(3, n, H, T)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    dev = {key: torch.from_numpy(d[key]).to("cuda").to(dt) for key in ("q", "k", "v")}
+    for key in ("alpha", "beta"):
+        dev[key] = torch.from_numpy(d[key]).to("cuda")
+    del d
+    log(f"[bench] staged prefill inputs ({'bf16' if bf16 else 'fp32'}) in {time.time() - t0:.1f}s")
+    pool = binding.StatePool(binding.FMT_I8F16, n, H, inputs.protected_perm(3, H),
+                             inputs.smoothing(3, H, False))
+    slots = torch.arange(n, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, T, H, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        pool.prefill(slots, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"],
+                     chunk=PREFILL_CHUNK, init_from_pool=False, out=out)
+
+    call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    secs = start.elapsed_time(end) / 1e3 / reps
+    ok = bool(torch.isfinite(out).all().item())
+    flop = n * H * (T // PREFILL_CHUNK) * PREFILL_FLOP_PER_CHUNK_HEAD
+    in_bytes = 3 * n * T * H * 128 * (2 if bf16 else 4) + 2 * n * T * H * 4
+    hbm = in_bytes + n * T * H * 128 * 4 + n * H * (T // PREFILL_CHUNK) * 20224
+    pool.close()
+    del pool, dev, out
+    torch.cuda.empty_cache()
+    return secs, {"ms_per_call": secs * 1e3, "tokens_per_s": n * T / secs,
+                  "tflops_fp32_mfma": flop / secs / 1e12,
+                  "frac_of_fp32_mfma_peak": flop / secs / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+                  "hbm_gbs_algorithmic": hbm / secs / 1e9, "flop_per_call": flop,
+                  "finite_outputs": ok,
+                  "workload": f"prefill {n} x {H} heads x {T} tokens, chunk {PREFILL_CHUNK}, "
+                              f"{'bf16' if bf16 else 'fp32'} q/k/v, zero initial state"}
+
+
 def cpu_baseline(inputs, kind, budget_s=12.0):
     """Oracle on a bounded sample of the same workload: all 256 slots x 32
     heads, the first consecutive steps that fit in about `budget_s` seconds
@@ -182,7 +245,7 @@ def main():
                     help="slot sets rotated per step (4 = cache-cold working set)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gdn", "kda", "f32", "all"], default="all")
+    ap.add_argument("--only", choices=["gdn", "kda", "f32", "prefill", "all"], default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -245,6 +308,14 @@ def main():
             log(f"[bench] kda pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
         del kda_in
 
+    prefill = {}
+    if args.only in ("prefill", "all"):
+        for bf16 in (False, True):
+            secs, st = run_prefill(torch, binding, inputs, bf16)
+            prefill["bf16" if bf16 else "fp32"] = st
+            log(f"[bench] prefill {'bf16' if bf16 else 'fp32'}: {secs * 1e3:.3f} ms/call, "
+                f"{st['tflops_fp32_mfma']:.1f} TFLOP/s fp32 mfma")
+
     def rate(key, nbytes):
         secs, ok = res[key]
         per_step = secs / steps
@@ -252,6 +323,19 @@ def main():
         return {"us_per_step": per_step * 1e6, "updates_per_s": ups,
                 "gbs": ups * nbytes / 1e9, "frac_of_peak": ups * nbytes / 1e9 / PEAK_HBM_GBS,
                 "finite_outputs": ok}
+
+    if not res:   # --only prefill: a diagnostic line for the prefill kernel alone
+        st = prefill["fp32"]
+        print(json.dumps({"metric": "prefill tokens/s (chunked, compressed state)",
+                          "value": st["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+                          "config": {"workload": st["workload"]},
+                          "roofline": {"bound": "mfma",
+                                       "achieved": st["tflops_fp32_mfma"],
+                                       "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": st["frac_of_fp32_mfma_peak"], "traffic": None},
+                          "detail": {"prefill": prefill}}))
+        return
 
     out = {}
     head_key = ("gdn", args.pools) if ("gdn", args.pools) in res else next(iter(res))
@@ -264,6 +348,8 @@ def main():
         detail[f"{key[0]}_pools{key[1]}"] = rate(key, nb)
     if ("gdn", 1) in res and ("f32", 1) in res:
         detail["speedup_vs_fp32_state"] = res[("f32", 1)][0] / res[("gdn", 1)][0]
+    if prefill:
+        detail["prefill"] = prefill
 
     cpu = None
     if not args.no_cpu_baseline:

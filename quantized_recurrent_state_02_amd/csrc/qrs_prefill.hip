@@ -75,13 +75,15 @@ __device__ __forceinline__ float ratio(const PrefillSmem &s, int t, int i) {
     return expf((float)(s.lg[t] - s.lg[i]));
 }
 
+// One input element at byte offset off of a buffer (zero outside its range);
+// bf16 widens exactly to FP32.
 template <int IN_BF16>
-__device__ __forceinline__ float ld_in(const void *p, size_t idx) {
+__device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, int off) {
     if (IN_BF16) {
-        const uint16_t bits = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p) + idx);
+        const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kStream);
         return __builtin_bit_cast(float, (uint32_t)bits << 16);
     }
-    return __builtin_nontemporal_load(reinterpret_cast<const float *>(p) + idx);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStream));
 }
 
 // 16x16 tile of the masked Gram matrix  A[t][i] = r(t, i) * (X_t . K_i)  for
@@ -159,8 +161,14 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
     if (init_from_pool) {
         if (FMT == 1) {
             uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
-            for (int e = tid; e < UNIT_BYTES / 16; e += PT)
-                reinterpret_cast<U4 *>(stg)[e] = reinterpret_cast<const U4 *>(unit)[e];
+            const __amdgpu_buffer_rsrc_t ru = make_rsrc(unit, UNIT_BYTES);
+            U4 part[(UNIT_BYTES / 16 + PT - 1) / PT];
+#pragma unroll
+            for (int i = 0; i < (UNIT_BYTES / 16 + PT - 1) / PT; ++i)
+                part[i] = buf_load16(ru, (tid + PT * i) * 16, 0);   // past the unit: zeros
+#pragma unroll
+            for (int i = 0; i < (UNIT_BYTES / 16 + PT - 1) / PT; ++i)
+                if (tid + PT * i < UNIT_BYTES / 16) reinterpret_cast<U4 *>(stg)[tid + PT * i] = part[i];
             __syncthreads();
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb)
@@ -197,19 +205,34 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         const int t0 = ch * chunk;
         const int ceff = min(chunk, T - t0);
 
-        // ---- 1. chunk operands into LDS (tokens >= ceff are zero, alpha 1) ----
-        for (int e = tid; e < CT * DK; e += PT) {
-            const int t = e >> 7;
-            float kv = 0.f, qv = 0.f, vv = 0.f;
-            if (t < ceff) {
-                const size_t base = (((size_t)b * T + (t0 + t)) * H + h) * DK;
-                kv = ld_in<IN_BF16>(k, base + perm_col);
-                qv = ld_in<IN_BF16>(q, base + perm_col);
-                vv = ld_in<IN_BF16>(v, base + in_col) / c_in;  // v' = D_c^{-1} v
+        // ---- 1. chunk operands into LDS.  Each input is read through a buffer
+        //      resource that ends at the chunk's last real token, so rows
+        //      t >= ceff read as zero (and alpha as 1 below); all 96 loads of a
+        //      thread are issued before the first LDS store. ----
+        {
+            constexpr int ESZ = IN_BF16 ? 2 : 4;
+            const size_t row0 = ((size_t)b * T + t0) * H + h;         // token t0 of (b, h)
+            const int rstride = H * DK * ESZ;                         // bytes between tokens
+            const int bytes = (ceff - 1) * rstride + DK * ESZ;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t *)k + row0 * DK * ESZ, bytes);
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t *)q + row0 * DK * ESZ, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t *)v + row0 * DK * ESZ, bytes);
+            const int t_first = tid >> 7;                             // rows t_first + 2 i
+            float kv[CT / 2], qv[CT / 2], vv[CT / 2];
+#pragma unroll
+            for (int i = 0; i < CT / 2; ++i) {
+                const int t = t_first + 2 * i;
+                kv[i] = ld_buf<IN_BF16>(rk, t * rstride + perm_col * ESZ);
+                qv[i] = ld_buf<IN_BF16>(rq, t * rstride + perm_col * ESZ);
+                vv[i] = ld_buf<IN_BF16>(rv, t * rstride + in_col * ESZ);
             }
-            s.K[t * LDK + in_col] = kv;
-            s.Q[t * LDK + in_col] = qv;
-            s.VU[t * LDK + in_col] = vv;
+#pragma unroll
+            for (int i = 0; i < CT / 2; ++i) {
+                const int t = t_first + 2 * i;
+                s.K[t * LDK + in_col] = kv[i];
+                s.Q[t * LDK + in_col] = qv[i];
+                s.VU[t * LDK + in_col] = vv[i] / c_in;  // v' = D_c^{-1} v
+            }
         }
         // ---- 2. decay prefix sums (wave 0: lane = token) ----
         if (tid < CT) {
@@ -302,60 +325,66 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         }
         __syncthreads();
 
-        // ---- 6. per wave: Delta = U - W S0 ----
+        // ---- 6. per wave: Delta = U - W S0 (both column tiles per A read) ----
         v4f D[4][2];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb) {
+            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < 8; ++kb) {
+                const v4f a = lds4(s.W + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    const v4f a = lds4(s.W + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
-                    acc = mfma4(a.x, S[kb][cb][0], acc);
-                    acc = mfma4(a.y, S[kb][cb][1], acc);
-                    acc = mfma4(a.z, S[kb][cb][2], acc);
-                    acc = mfma4(a.w, S[kb][cb][3], acc);
+                for (int j = 0; j < 4; ++j) {
+                    acc0 = mfma4(a[j], S[kb][0][j], acc0);
+                    acc1 = mfma4(a[j], S[kb][1][j], acc1);
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    D[tb][cb][r] =
-                        s.VU[(16 * tb + 4 * g + r) * LDK + 32 * w + 16 * cb + l16] - acc[r];
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float *u = s.VU + (16 * tb + 4 * g + r) * LDK + 32 * w + l16;
+                D[tb][0][r] = u[0] - acc0[r];
+                D[tb][1][r] = u[16] - acc1[r];
+            }
+        }
 
         // ---- 7. O = Gamma Q S0 + A_qk Delta, written as o = c (.) O ----
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb) {
+            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < 8; ++kb) {
+                const v4f a = lds4(s.Q + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    const v4f a = lds4(s.Q + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
-                    acc = mfma4(a.x, S[kb][cb][0], acc);
-                    acc = mfma4(a.y, S[kb][cb][1], acc);
-                    acc = mfma4(a.z, S[kb][cb][2], acc);
-                    acc = mfma4(a.w, S[kb][cb][3], acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] *= s.gam[16 * tb + 4 * g + r];
-#pragma unroll
-                for (int sb = 0; sb <= tb; ++sb) {
-                    const v4f a = lds4(s.M + (16 * tb + l16) * LDM + 16 * sb + 4 * g);
-                    acc = mfma4(a.x, D[sb][cb][0], acc);
-                    acc = mfma4(a.y, D[sb][cb][1], acc);
-                    acc = mfma4(a.z, D[sb][cb][2], acc);
-                    acc = mfma4(a.w, D[sb][cb][3], acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * tb + 4 * g + r;
-                    if (t < ceff)
-                        __builtin_nontemporal_store(
-                            c_out[cb] * acc[r],
-                            o + (((size_t)b * T + (t0 + t)) * H + h) * DV + 32 * w + 16 * cb + l16);
+                for (int j = 0; j < 4; ++j) {
+                    acc0 = mfma4(a[j], S[kb][0][j], acc0);
+                    acc1 = mfma4(a[j], S[kb][1][j], acc1);
                 }
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float gm = s.gam[16 * tb + 4 * g + r];
+                acc0[r] *= gm;
+                acc1[r] *= gm;
+            }
+#pragma unroll
+            for (int sb = 0; sb <= tb; ++sb) {
+                const v4f a = lds4(s.M + (16 * tb + l16) * LDM + 16 * sb + 4 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc0 = mfma4(a[j], D[sb][0][j], acc0);
+                    acc1 = mfma4(a[j], D[sb][1][j], acc1);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tb + 4 * g + r;
+                if (t < ceff) {
+                    float *op = o + (((size_t)b * T + (t0 + t)) * H + h) * DV + 32 * w + l16;
+                    __builtin_nontemporal_store(c_out[0] * acc0[r], op);
+                    __builtin_nontemporal_store(c_out[1] * acc1[r], op + 16);
+                }
+            }
+        }
 
         // ---- 8. S_C = g_C S0 + K^T diag(r(C, t)) Delta ----
         {
