@@ -1,8 +1,9 @@
 """Seeded synthetic inputs for the compressed-state decode workloads.
 
 This module only draws random numbers and shapes them; it holds none of the
-recurrence or codec arithmetic, imports only numpy, and is the one module that
-both the HIP path's tests/benchmark and the CPU oracle consume.
+recurrence or codec arithmetic, imports numpy (and torch, lazily, for the
+device-side draws of large workloads), and is the one module that both the
+HIP path's tests/benchmark and the CPU oracle consume.
 
 Every tensor comes from ``numpy.random.default_rng(SeedSequence([cfg,
 tensor_id, step]))`` (PCG64), is drawn and transformed in float64 and cast to
@@ -179,3 +180,65 @@ def paged_slots(cfg: int = 4, num_slots: int = 4096, active: int = 1024):
     r.shuffle(g)
     r.shuffle(k)
     return g, k
+
+
+# ---------------------------------------------------------------------------
+# Device-side draws of the same recipes (large workloads).  Each tensor uses a
+# torch generator on the device seeded from SeedSequence([cfg, tensor_id,
+# step]); values are drawn in float64, transformed, and cast to float32 once.
+# A caller that checks against the oracle copies the drawn arrays to the host.
+# ---------------------------------------------------------------------------
+
+def _torch_gen(cfg: int, tensor_id: int, step: int, device):
+    import torch
+
+    seed = int(np.random.SeedSequence([cfg, tensor_id, step]).generate_state(1, np.uint64)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed & ((1 << 63) - 1))
+    return g
+
+
+def initial_state_device(cfg: int, n: int, heads: int, perm: np.ndarray, first: int = 0,
+                         device="cuda"):
+    """Heavy-tailed model-space initial states on the device, float32
+    [n][H][128][128]: 0.1 * Student-t(3) (drawn as Z / sqrt(chi2_3 / 3), the
+    chi-square as a sum of three squared normals), with the head's first four
+    protected channels perm[h][0:4] multiplied by 20.  One generator per
+    request index first + b."""
+    import torch
+
+    out = torch.empty((n, heads, DK, DV), dtype=torch.float32, device=device)
+    rows = torch.as_tensor(np.asarray(perm)[:, :4].astype(np.int64), device=device)
+    for b in range(n):
+        g = _torch_gen(cfg, T_STATE, first + b, device)
+        z = torch.randn((heads, DK, DV), generator=g, dtype=torch.float64, device=device)
+        c2 = torch.randn((3, heads, DK, DV), generator=g, dtype=torch.float64,
+                         device=device).square().sum(0)
+        S = 0.1 * z / torch.sqrt(c2 / 3.0)
+        S[torch.arange(heads, device=device)[:, None], rows, :] *= 20.0
+        out[b] = S.to(torch.float32)
+    return out
+
+
+def step_inputs_device(cfg: int, step: int, n: int, heads: int, kind: str, device="cuda"):
+    """Per-step decode operands on the device, the recipe of step_inputs."""
+    import torch
+
+    def normal(tid, shape):
+        return torch.randn(shape, generator=_torch_gen(cfg, tid, step, device),
+                           dtype=torch.float64, device=device)
+
+    shp = (n, heads, DK)
+    q = normal(T_Q, shp)
+    k = normal(T_K, shp)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    out = dict(q=q.float(), k=k.float(), v=normal(T_V, (n, heads, DV)).float(),
+               beta=torch.sigmoid(normal(T_BETA, (n, heads))).float())
+    if kind == "gdn":
+        out["alpha"] = torch.exp(-torch.nn.functional.softplus(normal(T_GATE, (n, heads)) + 3.0)).float()
+    elif kind == "kda":
+        out["g"] = (-torch.nn.functional.softplus(normal(T_GATE, shp) + 2.0)).float()
+    else:
+        raise ValueError(kind)
+    return out

@@ -1,0 +1,137 @@
+"""Paged decode over a pool shared by GDN and KDA requests (the serving
+layout: one persistent packed state per request slot and head, DAMP arXiv
+HTML, Appendix A.5), against the oracle.
+
+4,096 slots x 32 heads (2,048 GDN-typed, 2,048 KDA-typed); 1,024 active
+requests (512 of each type, distinct random slot ids); 1,024 steps, each one
+GDN call and one KDA call on the same pool; heavy-tailed initial states with
+outlier rows in the FP16 channels; value smoothing on.  Inputs are drawn on
+the device (inputs.*_device) and the oracle receives the same arrays.
+
+Checks:
+* every inactive slot's bytes are identical to what was written before the
+  first step (the pool starts as seeded random bytes);
+* on 512 sampled units (8 GDN + 8 KDA slots x 32 heads), every 64th step and
+  the last: the per-step derived bounds on the stored state and the readout
+  (tests/parity_util.py), and on the final state the one-quantization-step bar
+  (INT8 codes at most one step apart; FP16 rows one ulp plus the coupling of
+  that step's INT8 differences through the rank-1 write).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_recurrent_state_02_amd import binding, inputs
+from tests.parity_util import (StepBound, dequant_units, describe_misses, north_star_step_ok,
+                               oracle_units, split_gpu, to_dev, ulp16)
+
+pytestmark = pytest.mark.gpu
+DK = DV = 128
+
+
+def _fill_random(pool, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    u = pool.units()
+    for i in range(0, u.shape[0], 4096):
+        blk = u[i:i + 4096]
+        blk.copy_(torch.randint(0, 256, blk.shape, generator=g, device="cuda", dtype=torch.int32)
+                  .to(torch.uint8))
+
+
+def _check_step(kind, bound, sub, gu, ou, Tprev_o, D):
+    """Per-step derived bounds for the sampled units of one kind; returns the
+    FP16 coupling allowance [U][16][128]."""
+    Tg = dequant_units(*gu).astype(np.float64)
+    To = dequant_units(*ou).astype(np.float64)
+    Dn = Tg - To
+    coupling = np.zeros((Tg.shape[0], 16, DV))
+    H = sub["q"].shape[1]
+    gate = sub["alpha"] if kind == "gdn" else sub["g"]
+    for bi in range(sub["q"].shape[0]):
+        for h in range(H):
+            u = bi * H + h
+            kk, qq, lam, vp, beta = bound.operands(sub, bi, h, gate)
+            dx = bound.pre_bound(D[u], Tprev_o[u], kk, lam, vp, beta)
+            coupling[u] = dx[:16]
+            lim = dx.copy()
+            lim[16:] += np.repeat(np.maximum(gu[2][u], ou[2][u]), 32, axis=1) * (1 + 2.0 ** -15)
+            lim[:16] += ulp16(np.maximum(np.abs(Tg[u, :16]), np.abs(To[u, :16])))
+            assert np.all(np.abs(Dn[u]) <= lim), f"{kind} unit {u}: state outside derived bound"
+            Tpre = lam[:, None] * Tprev_o[u] + np.outer(kk, beta * (vp - (kk * lam) @ Tprev_o[u]))
+            lim_o = bound.c[h] * (np.abs(qq) @ dx + 2.0 ** -20 * 130 * (np.abs(qq) @ np.abs(Tpre))) \
+                + 1e-30
+            ro = np.abs(sub["o_gpu"][bi, h] - sub["o_orc"][bi, h]) / lim_o
+            assert ro.max() <= 1.0, f"{kind} unit {u}: readout outside derived bound"
+    return coupling, Tg, To
+
+
+def test_paged_mixed_pool():
+    cfg, H, num_slots, steps = 4, 32, 4096, 1024
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    gdn_slots, kda_slots = inputs.paged_slots(cfg, num_slots, 1024)
+    gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    _fill_random(gp, 404)
+    active = np.concatenate([gdn_slots, kda_slots])
+    # heavy-tailed initial states of the active requests (request index = position)
+    for i in range(0, len(active), 64):
+        S = inputs.initial_state_device(cfg, min(64, len(active) - i), H, perm, first=i)
+        gp.store(to_dev(active[i:i + 64], torch.int32), S)
+    torch.cuda.synchronize()
+    initial = gp.units().clone()
+    inactive = np.setdiff1d(np.arange(num_slots), active)
+
+    rs = np.random.default_rng(44)
+    samp = {"gdn": np.sort(rs.choice(len(gdn_slots), 8, replace=False)),
+            "kda": np.sort(rs.choice(len(kda_slots), 8, replace=False))}
+    slots_of = {"gdn": gdn_slots, "kda": kda_slots}
+    # the oracle holds only the sampled slots: GDN at local ids 0..7, KDA at 8..15
+    local = {"gdn": np.arange(8, dtype=np.int32), "kda": 8 + np.arange(8, dtype=np.int32)}
+    op = oracle.OraclePool(16, H, perm, c)
+    for kind in ("gdn", "kda"):
+        hi, lo, sc = split_gpu(gp, slots_of[kind][samp[kind]])
+        idx = (local[kind][:, None] * H + np.arange(H)[None, :]).ravel()
+        op.hi[idx], op.lo[idx], op.sc[idx] = hi, lo, sc
+    bounds = {kind: StepBound(perm, c, kind) for kind in ("gdn", "kda")}
+    dslots = {kind: to_dev(slots_of[kind], torch.int32) for kind in ("gdn", "kda")}
+    D = {kind: np.zeros((8 * H, DK, DV)) for kind in ("gdn", "kda")}
+    checked = 0
+    for t in range(steps):
+        check = (t % 64 == 63) or t == steps - 1
+        for kind in ("gdn", "kda"):
+            d = inputs.step_inputs_device(cfg, t, len(slots_of[kind]), H, kind)
+            sl = slots_of[kind][samp[kind]]
+            if check:
+                gprev = split_gpu(gp, sl)
+                Tprev_o = dequant_units(*oracle_units(op, local[kind])).astype(np.float64)
+                D[kind] = dequant_units(*gprev).astype(np.float64) - Tprev_o
+            fn = gp.gdn_step if kind == "gdn" else gp.kda_step
+            gate = d["alpha"] if kind == "gdn" else d["g"]
+            og = fn(dslots[kind], d["q"], d["k"], d["v"], gate, d["beta"])
+            sub = {key: val[torch.as_tensor(samp[kind], device="cuda")].cpu().numpy()
+                   for key, val in d.items()}
+            oo = op.decode_step(local[kind], sub["q"], sub["k"], sub["v"],
+                                sub["alpha"] if kind == "gdn" else sub["g"], sub["beta"],
+                                0 if kind == "gdn" else 1)
+            if check:
+                sub["o_gpu"] = og[torch.as_tensor(samp[kind], device="cuda")].cpu().numpy()
+                sub["o_orc"] = oo
+                gu, ou = split_gpu(gp, sl), oracle_units(op, local[kind])
+                coupling, Tg, To = _check_step(kind, bounds[kind], sub, gu, ou, Tprev_o, D[kind])
+                checked += 1
+                if t == steps - 1:
+                    ok_lo, ok_hi, _, _ = north_star_step_ok(Tg, To, gu[2], ou[2], coupling)
+                    assert ok_lo.all() and ok_hi.all(), (
+                        f"{kind} final state: {(~ok_lo).sum()} INT8 / {(~ok_hi).sum()} FP16 beyond "
+                        "one step: " + describe_misses(ok_lo, Tg, To, gu[2], ou[2]))
+    torch.cuda.synchronize()
+    # untouched slots
+    u_now = gp.units().view(num_slots, H, -1)
+    u0 = initial.view(num_slots, H, -1)
+    ia = torch.as_tensor(inactive, device="cuda")
+    for i in range(0, len(inactive), 512):
+        sel = ia[i:i + 512]
+        assert torch.equal(u_now[sel], u0[sel]), "an inactive slot changed"
+    assert checked == 2 * 16
