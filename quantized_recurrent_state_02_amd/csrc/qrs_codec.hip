@@ -62,7 +62,7 @@ __global__ __launch_bounds__(THREADS) void store_i8f16_kernel(PoolView pool,
         uint32_t hw[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-            hw[c] = f32_to_f16_bits(x[0][2 * c]) | (f32_to_f16_bits(x[0][2 * c + 1]) << 16);
+            hw[c] = pack_f16x2(x[0][2 * c], x[0][2 * c + 1]);
         V4 *hp = reinterpret_cast<V4 *>(unit + HI_OFF + rg * (DV * 2) + cb * 32);
         hp[0] = V4{hw[0], hw[1], hw[2], hw[3]};
         hp[1] = V4{hw[4], hw[5], hw[6], hw[7]};
@@ -72,9 +72,9 @@ __global__ __launch_bounds__(THREADS) void store_i8f16_kernel(PoolView pool,
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(x[r][c]));
-        amax = fmaxf(amax, partner_xor1(amax));
+        amax = pair_max(amax);
         const float s = group_scale(amax);
-        const double rinv = scale_reciprocal(s);
+        const double rinv = pack_reciprocal(s);
         V4 cw;
         cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
         cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);

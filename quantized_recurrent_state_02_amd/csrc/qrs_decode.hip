@@ -20,14 +20,17 @@
 //
 // Cost model (gfx950): every byte of the unit is read once and written once
 // with 128-bit buffer accesses (non-temporal, except the FP16-row stores, see
-// below).  The VALU work is about eleven instructions per state value:
-// convert, scale, two reduction FMAs, the update FMA, half an absmax, a
+// below).  The VALU work is about 10.6 instructions per state value: convert,
+// scale, two reduction FMAs, the update FMA, half an absmax, a
 // four-instruction exact quantizer whose last step also packs the code byte,
-// and per-row / per-unit overheads.  Four workgroups fit per CU (176 VGPRs);
+// and per-row / per-unit overheads.  Four workgroups fit per CU (179 VGPRs);
 // the grid is one workgroup per unit, so the hardware refills CUs as units
-// finish.  Persistent workgroups that prefetch their next unit into registers
-// measured slower: loads and stores share one wait counter on gfx9, so every
-// iteration also waited for the previous unit's stores.
+// finish.  On MI355X the step time follows the VALU count (a kernel with a
+// cheaper, inexact quantizer ran 7% faster), while changes to the memory side
+// alone did not move it: workgroups that prefetch a second unit, fewer or
+// more resident workgroups, one wave per column half over a layout with
+// contiguous column halves, and single 16-byte scale accesses all measured
+// the same or slower.
 #include "qrs_internal.h"
 
 namespace qrs {
@@ -127,8 +130,8 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
                                 hi_raw[1].x, hi_raw[1].y, hi_raw[1].z, hi_raw[1].w};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            x[0][2 * c] = dr[0] * f16_bits_to_f32(hw[c] & 0xffffu);
-            x[0][2 * c + 1] = dr[0] * f16_bits_to_f32(hw[c] >> 16);
+            x[0][2 * c] = mul_f16lo(dr[0], hw[c]);
+            x[0][2 * c + 1] = mul_f16hi(dr[0], hw[c]);
         }
     }
 #pragma unroll
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
         for (int c = 0; c < 8; ++c) {
             const float e0 = __builtin_fmaf(kr[0], bdc[2 * c], x[0][2 * c]);
             const float e1 = __builtin_fmaf(kr[0], bdc[2 * c + 1], x[0][2 * c + 1]);
-            hw[c] = f32_to_f16_bits(e0) | (f32_to_f16_bits(e1) << 16);
+            hw[c] = pack_f16x2(e0, e1);
         }
         // Each store instruction covers only every other 16 B of the FP16
         // rows, so these two use the default cache policy and meet in L2;
@@ -210,9 +213,9 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
             x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
             amax = fmaxf(amax, fabsf(x[r][c]));
         }
-        amax = fmaxf(amax, partner_xor1(amax));
+        amax = pair_max(amax);
         const float s = group_scale(amax);
-        const double rinv = scale_reciprocal(s);
+        const double rinv = pack_reciprocal(s);
         U4 cw;
         cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
         cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);

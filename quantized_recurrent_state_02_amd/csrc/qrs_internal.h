@@ -59,10 +59,18 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// Value of the partner lane tid ^ 1 (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ float partner_xor1(float x) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+// max(a, a of the partner lane tid ^ 1) for a >= 0 (a group maximum of
+// absolute values): non-negative IEEE floats order like their bit patterns,
+// so one v_max_u32 with a DPP quad_perm [1,0,3,2] source does it.  The
+// s_nop gives the two wait states a DPP read needs after a VALU write of its
+// source register.
+__device__ __forceinline__ float pair_max(float a) {
+    uint32_t d;
+    asm("s_nop 1\n\tv_max_u32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf "
+        "bound_ctrl:1"
+        : "=v"(d)
+        : "v"(__builtin_bit_cast(uint32_t, a)));
+    return __builtin_bit_cast(float, d);
 }
 
 // Scale of a group: RN32(amax / 127).  Evaluated as RN32(RN64(amax * RN64(1/127))):
@@ -83,6 +91,27 @@ __device__ __forceinline__ double scale_reciprocal(float s) {
     e = __builtin_fma(-sd, r, 1.0);
     r = __builtin_fma(r, e, r);
     return s == 0.0f ? 0.0 : r;
+}
+
+// scale_reciprocal for the packing quantizer (quant4): a zero scale is first
+// raised to 2^-1000 (one integer max on the high word of the FP64 value, in
+// place of a compare and two selects), so its reciprocal is 2^1000.  A group
+// with s = 0 then still gets code 0 everywhere: zero values give 0, and the
+// nonzero values of a group whose amax / 127 underflowed to zero give an
+// infinite quotient, whose packed low byte is 0.  Nonzero scales are at least
+// 2^-149 and pass unchanged.
+__device__ __forceinline__ double pack_reciprocal(float s) {
+    const uint64_t bits = __builtin_bit_cast(uint64_t, (double)s);
+    const uint32_t floor_hi = 0x01700000u;  // high word of 2^-1000
+    uint32_t hi;
+    asm("v_max_u32 %0, %1, %2" : "=v"(hi) : "v"((uint32_t)(bits >> 32)), "v"(floor_hi));
+    const double sd = __builtin_bit_cast(double, ((uint64_t)hi << 32) | (uint32_t)bits);
+    double r = __builtin_amdgcn_rcp(sd);
+    double e = __builtin_fma(-sd, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-sd, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    return r;
 }
 
 // RN32(x / s) for a group with reciprocal rinv.  The FP64 product is within
@@ -130,6 +159,30 @@ __device__ __forceinline__ uint32_t pack4_codes(float y0, float y1, float y2, fl
 __device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3, double rinv) {
     return pack4_codes(quant_quotient(x0, rinv), quant_quotient(x1, rinv),
                        quant_quotient(x2, rinv), quant_quotient(x3, rinv));
+}
+
+// Two FP32 values to packed IEEE binary16 (lo -> bits [15:0], hi -> bits
+// [31:16]), each rounded to nearest even: the same results as f32_to_f16_bits.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    uint32_t d;
+    asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
+    return d;
+}
+
+// a * f32(binary16 in the low / high half of w) with one rounding, as a
+// mixed-precision fma whose addend is -0 (x + (-0) = x for every x, the sign
+// of zero included), so the result equals the FP32 product a * f32(h).
+__device__ __forceinline__ float mul_f16lo(float a, uint32_t w) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(w), "v"(-0.0f));
+    return d;
+}
+__device__ __forceinline__ float mul_f16hi(float a, uint32_t w) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+        : "=v"(d)
+        : "v"(a), "v"(w), "v"(-0.0f));
+    return d;
 }
 
 __device__ __forceinline__ float sext_byte_to_f32(uint32_t w, int b) {
