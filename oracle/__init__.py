@@ -58,6 +58,7 @@ def load():
     lib.orc_f32_decode.argtypes = [p, i, p, p, p, i, i, p, p, p, p, p, p]
     lib.orc_f64_decode.argtypes = [p, i, p, p, p, i, i, p, p, p, p, p, p]
     lib.orc_i8_prefill.argtypes = [p, p, p, i, p, p, p, i, i, i, p, p, p, p, p, p, i]
+    lib.orc_channel_error.argtypes = [p, i, i, p, p]
     lib.orc_unit_bytes.argtypes = []
     lib.orc_unit_bytes.restype = i64
     _lib = lib

@@ -446,6 +446,46 @@ void orc_i8_prefill(uint16_t *hi, int8_t *lo, float *sc, int num_heads, const in
 }
 
 /* Sizes of the oracle's representation of one unit, in bytes. */
+/* ------------------------------------------------------------------ */
+/* Key-channel selection: quantization-error energy of each key channel */
+/* ([DAMP] section 4 "Accumulated-error risk", Eq.(8), and Appendix A.2 */
+/* Eq.(14); [DAMP2] section 2.5, e_{t,u}).                              */
+/* ------------------------------------------------------------------ */
+
+/* For n calibration states S [n][H][DK][DV] in model coordinates, the squared
+ * error of row u under the low-precision storage mapping: the row is taken to
+ * stored value coordinates (x_j = S[u][j] / c[j], FP32 divide), every 32-value
+ * group is quantized and dequantized with the INT8 codec above, the result is
+ * mapped back (x_hat_j * c[j], FP32 multiply), and
+ *     e[n][H][u] = sum_j (x_hat_j c_j - S[u][j])^2
+ * is accumulated in FP64 over increasing j.  Every key channel is measured
+ * under the INT8 mapping, since the statistic ranks candidates for the FP16
+ * tier.  c == NULL means unit smoothing. */
+void orc_channel_error(const float *S, int n, int num_heads, const float *c, double *e)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t sh = 0; sh < (int64_t)n * num_heads; ++sh) {
+        const int h = (int)(sh % num_heads);
+        const float *Su = S + sh * DK * DV;
+        for (int u = 0; u < DK; ++u) {
+            float x[DV];
+            int8_t code[DV];
+            float sc[NGRP];
+            for (int j = 0; j < DV; ++j)
+                x[j] = Su[u * DV + j] / (c ? c[h * DV + j] : 1.0f);
+            for (int g = 0; g < NGRP; ++g)
+                orc_quantize_group(&x[g * GRP], GRP, &code[g * GRP], &sc[g]);
+            double acc = 0.0;
+            for (int j = 0; j < DV; ++j) {
+                const float back = dequant_code(sc[j / GRP], code[j]) * (c ? c[h * DV + j] : 1.0f);
+                const double d = (double)back - (double)Su[u * DV + j];
+                acc += d * d;
+            }
+            e[sh * DK + u] = acc;
+        }
+    }
+}
+
 int64_t orc_unit_bytes(void)
 {
     return (int64_t)KHI * DV * 2 + (int64_t)KLO * DV * 1 + (int64_t)KLO * NGRP * 4;
