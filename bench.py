@@ -26,7 +26,7 @@ timed on a bounded sample of the same workload.
 `detail` also reports KDA decode, the single-pool variants, the FP32-state
 kernel on the same inputs, and the chunked prefill kernel (8 x 32 heads x
 4096 tokens, chunks of 64, FP32 and bf16 q/k/v) against the FP32 matrix-core
-peak.
+peak, and the key-channel selection kernels on a calibration-shaped sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -194,6 +194,74 @@ def run_prefill(torch, binding, inputs, bf16, reps=3):
                               f"{'bf16' if bf16 else 'fp32'} q/k/v, zero initial state"}
 
 
+# Key-channel selection, calibration-shaped: 32 sequences of 256 steps, 32
+# heads, one sampled state every 8 steps (1,024 samples per head).  The error
+# kernel reads every sampled FP32 state once (64 KiB per sample and head).
+SELECT_SEQ, SELECT_T, SELECT_EVERY = 32, 256, 8
+
+
+def run_select(torch, binding, H, reps=3):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    n_seq, T = SELECT_SEQ, SELECT_T
+    seqs = torch.arange(n_seq, dtype=torch.int32, device="cuda").repeat_interleave(T // SELECT_EVERY)
+    ts = torch.arange(SELECT_EVERY - 1, T, SELECT_EVERY, dtype=torch.int32,
+                      device="cuda").repeat(n_seq)
+    n = seqs.numel()
+    S = 0.1 * torch.randn((n, H, 128, 128), generator=g, device="cuda", dtype=torch.float32)
+    a = 0.5 + 0.5 * torch.rand((n_seq, T, H, 128), generator=g, device="cuda", dtype=torch.float32)
+    c = torch.exp(torch.empty((H, 128), device="cuda").uniform_(-0.69, 0.69, generator=g))
+    w = torch.full((n,), 1.0 / n, dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            r = fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps, r
+
+    t_err, e = timed(lambda: binding.channel_error(S, c))
+    t_win, W = timed(lambda: binding.persistence_window(a, seqs, ts, 256))
+    t_geo, P = timed(lambda: binding.persistence_geometric(a, seqs, ts, w, 1e-4))
+    t_sw, C = timed(lambda: binding.channel_scores(e, w, W=W))
+    t_sp, _ = timed(lambda: binding.channel_scores(e, w, P=P))
+    t0 = time.perf_counter()
+    perm = binding.select_protected_channels(C)
+    t_sel = time.perf_counter() - t0
+    ok = bool(torch.isfinite(C).all().item()) and perm.shape == (H, 128)
+    err_bytes = n * H * (128 * 128 * 4 + 128 * 8)
+    del S, a
+    torch.cuda.empty_cache()
+    return {"workload": f"{n_seq} sequences x {T} steps x {H} heads, a state every "
+                        f"{SELECT_EVERY} steps ({n} samples), window 256",
+            "channel_error_ms": t_err * 1e3, "channel_error_gbs": err_bytes / t_err / 1e9,
+            "channel_error_frac_of_peak": err_bytes / t_err / 1e9 / PEAK_HBM_GBS,
+            "persistence_window_ms": t_win * 1e3, "persistence_geometric_ms": t_geo * 1e3,
+            "scores_window_ms": t_sw * 1e3, "scores_geometric_ms": t_sp * 1e3,
+            "select_host_ms": t_sel * 1e3, "finite": ok}
+
+
+def cpu_select_baseline(H, samples=48):
+    """The oracle's channel-error step on a bounded sample (samples x H states)."""
+    from oracle import selector
+
+    r = np.random.default_rng(5)
+    S = (0.1 * r.standard_normal((samples, H, 128, 128))).astype(np.float32)
+    c = np.exp(r.uniform(-0.69, 0.69, (H, 128))).astype(np.float32)
+    t0 = time.perf_counter()
+    selector.channel_error(S, c)
+    dt = time.perf_counter() - t0
+    return {"channel_error_samples_per_s": samples / dt,
+            "sample": f"{samples} states x {H} heads", "seconds": dt,
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))}
+
+
 def cpu_baseline(inputs, kind, budget_s=12.0):
     """Oracle on a bounded sample of the same workload: all 256 slots x 32
     heads, the first consecutive steps that fit in about `budget_s` seconds
@@ -245,7 +313,8 @@ def main():
                     help="slot sets rotated per step (4 = cache-cold working set)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gdn", "kda", "f32", "prefill", "all"], default="all")
+    ap.add_argument("--only", choices=["gdn", "kda", "f32", "prefill", "select", "all"],
+                    default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -316,6 +385,14 @@ def main():
             log(f"[bench] prefill {'bf16' if bf16 else 'fp32'}: {secs * 1e3:.3f} ms/call, "
                 f"{st['tflops_fp32_mfma']:.1f} TFLOP/s fp32 mfma")
 
+    select = {}
+    if args.only in ("select", "all"):
+        select = run_select(torch, binding, H)
+        log(f"[bench] channel selection: error {select['channel_error_ms']:.3f} ms "
+            f"({select['channel_error_gbs']:.0f} GB/s), window {select['persistence_window_ms']:.3f} ms")
+        if not args.no_cpu_baseline:
+            select["cpu_oracle"] = cpu_select_baseline(H)
+
     def rate(key, nbytes):
         secs, ok = res[key]
         per_step = secs / steps
@@ -324,6 +401,18 @@ def main():
                 "gbs": ups * nbytes / 1e9, "frac_of_peak": ups * nbytes / 1e9 / PEAK_HBM_GBS,
                 "finite_outputs": ok}
 
+    if not res and select:   # --only select: a diagnostic line for the selection kernels
+        print(json.dumps({"metric": "key-channel selection: calibration states scored per second",
+                          "value": 1024 / (select["channel_error_ms"] / 1e3),
+                          "unit": "samples/s", "n_gpus": 1, "higher_is_better": True,
+                          "dtype": "f32", "data": "synthetic",
+                          "config": {"workload": select["workload"]},
+                          "roofline": {"bound": "hbm", "achieved": select["channel_error_gbs"],
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": select["channel_error_frac_of_peak"],
+                                       "traffic": None},
+                          "detail": {"select": select}}))
+        return
     if not res:   # --only prefill: a diagnostic line for the prefill kernel alone
         st = prefill["fp32"]
         print(json.dumps({"metric": "prefill tokens/s (chunked, compressed state)",
@@ -350,6 +439,8 @@ def main():
         detail["speedup_vs_fp32_state"] = res[("f32", 1)][0] / res[("gdn", 1)][0]
     if prefill:
         detail["prefill"] = prefill
+    if select:
+        detail["select"] = select
 
     cpu = None
     if not args.no_cpu_baseline:

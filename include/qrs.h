@@ -190,6 +190,78 @@ int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int c
                         const float *alpha, const float *beta, float *o, int init_from_pool,
                         hipStream_t stream);
 
+/*
+ * Key-channel selection: the offline construction of perm (DAMP arXiv HTML,
+ * section 4 "Key-channel budget", "Accumulated-error risk", "Budgeted
+ * selection", Eqs.(7)-(10); Appendix A.2 Eqs.(13)-(15); Appendix A.4
+ * Algorithm 1; v2 reading notes, section 2.5).  Calibration statistics come
+ * from FP32 state trajectories; the result is the perm of
+ * qrs_create_state_pool.  These calls need no pool and run on the current
+ * device.
+ */
+
+/*
+ * Quantization-error energy of every key channel of n calibration states
+ * (Eq.(14) integrand; v2 notes e_{t,u}):
+ *   S: FP32 [n][H][128][128], model coordinates, 16-byte aligned;
+ *   smooth: FP32 [H][128] value-column scales c (NULL = ones), 16-byte aligned;
+ *   e: FP64 [n][H][128] output,
+ *   e[s][h][u] = sum_j (Q(S[s][h][u][j] / c[h][j]) * c[h][j] - S[s][h][u][j])^2
+ * where Q quantizes and dequantizes each 32-value group with the INT8 codec of
+ * qrs_store_state (every row is measured under INT8, the tier the selection
+ * protects channels from).  The squares are summed in FP64.
+ */
+int qrs_channel_error(int n, int num_heads, const float *S, const float *smooth, double *e,
+                      hipStream_t stream);
+
+/*
+ * Finite-horizon persistence weight of each sampled state write (v2 notes
+ * section 2.5):
+ *   W[s][h][u] = 1 + sum_{j=1..horizon} prod_{r=1..j} a[q][t+r][h][u]^2,
+ * with q = sample_seq[s], t = sample_t[s]; the sum stops at the end of the
+ * trajectory (t + j <= T - 1).
+ *   a: FP32 [n_seq][T][H][128] per-step decays (GDN: alpha repeated over
+ *      the key channels; KDA: exp(g));
+ *   sample_seq, sample_t: int32 [n] device arrays;  W: FP64 [n][H][128].
+ * A sample whose sequence or step is out of range gets NaN.  FP64 products
+ * and sums in step order.
+ */
+int qrs_persistence_window(int n_seq, int T, int num_heads, const float *a, int n,
+                           const int32_t *sample_seq, const int32_t *sample_t, int horizon,
+                           double *W, hipStream_t stream);
+
+/*
+ * Geometric-mean persistence (Eq.(15)):
+ *   a_eff[h][u] = exp(sum_s weight[s] log a[q_s][t_s][h][u]),
+ *   P[h][u] = 1 / max(1 - a_eff^2, tau)    (the pages use tau = 1e-4),
+ * weight: FP64 [n] device (the domain-balanced mean of Eq.(13) has
+ * weight[s] = 1 / (|D| |Omega_d(s)|)); samples with weight 0 are skipped; an
+ * out-of-range sample makes its head's P NaN.  P: FP64 [H][128].
+ */
+int qrs_persistence_geometric(int n_seq, int T, int num_heads, const float *a, int n,
+                              const int32_t *sample_seq, const int32_t *sample_t,
+                              const double *weight, double tau, double *P, hipStream_t stream);
+
+/*
+ * Key-channel risk C: FP64 [H][128] (device), from e [n][H][128] and weight
+ * [n]; exactly one of W and P is given:
+ *   W (v2 notes):  C[h][u] = sum_s weight[s] e[s][h][u] W[s][h][u];
+ *   P (Eq.(10) with Eqs.(14)-(15)):  C[h][u] = (sum_s weight[s] e[s][h][u]) P[h][u].
+ * Sums run in sample order, without fused multiply-adds.
+ */
+int qrs_channel_scores(int n, int num_heads, const double *e, const double *W, const double *P,
+                       const double *weight, double *C, hipStream_t stream);
+
+/*
+ * Protected channels and the permutation (Algorithm 1), on the host:
+ * score_host FP64 [H][128] (host), perm_host int32 [H][128] (host output).
+ * Per head, the k_hi channels of largest score (equal scores: lower index
+ * first; NaN ranks last) are placed first, then the rest, each in ascending
+ * channel order.  k_hi is 16 for the pool formats of this library.
+ */
+int qrs_select_protected_channels(int num_heads, const double *score_host, int k_hi,
+                                  int32_t *perm_host);
+
 /* Name of a status code (static string). */
 const char *qrs_status_string(int status);
 

@@ -31,7 +31,9 @@ HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
 EXPORTED = (
     "qrs_state_pool_bytes", "qrs_create_state_pool", "qrs_destroy_state_pool", "qrs_pool_info",
     "qrs_store_state", "qrs_dequant_state", "qrs_gdn_decode_step", "qrs_kda_decode_step",
-    "qrs_chunked_prefill", "qrs_status_string",
+    "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
+    "qrs_persistence_geometric", "qrs_channel_scores", "qrs_select_protected_channels",
+    "qrs_status_string",
 )
 
 _lib = None
@@ -69,6 +71,16 @@ def load(path: str = LIB_PATH):
         fn.restype = i
     lib.qrs_chunked_prefill.argtypes = [p, p, i, i, i, i, p, p, p, p, p, p, i, p]
     lib.qrs_chunked_prefill.restype = i
+    lib.qrs_channel_error.argtypes = [i, i, p, p, p, p]
+    lib.qrs_channel_error.restype = i
+    lib.qrs_persistence_window.argtypes = [i, i, i, p, i, p, p, i, p, p]
+    lib.qrs_persistence_window.restype = i
+    lib.qrs_persistence_geometric.argtypes = [i, i, i, p, i, p, p, p, ctypes.c_double, p, p]
+    lib.qrs_persistence_geometric.restype = i
+    lib.qrs_channel_scores.argtypes = [i, i, p, p, p, p, p, p]
+    lib.qrs_channel_scores.restype = i
+    lib.qrs_select_protected_channels.argtypes = [i, p, i, p]
+    lib.qrs_select_protected_channels.restype = i
     lib.qrs_status_string.argtypes = [i]
     lib.qrs_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -221,3 +233,86 @@ def split_units(raw: np.ndarray):
     lo = raw[:, LO_OFFSET:SCALE_OFFSET].copy().view(np.int8).reshape(U, DK - KHI, DV)
     sc = raw[:, SCALE_OFFSET:].copy().view(np.float32).reshape(U, DK - KHI, DV // GRP)
     return hi, lo, sc
+
+
+# ---------------------------------------------------------------------------
+# key-channel selection (argument marshalling for the qrs_channel_* calls)
+# ---------------------------------------------------------------------------
+
+def _opt(t, dtype, shape, name):
+    return None if t is None else _dev(t, dtype, shape, name)
+
+
+def channel_error(S: torch.Tensor, smooth: torch.Tensor | None = None, out=None) -> torch.Tensor:
+    """qrs_channel_error: e [n][H][128] (float64) for calibration states
+    S [n][H][128][128] (float32, model coordinates) and smoothing c [H][128]."""
+    n, H = S.shape[0], S.shape[1]
+    if out is None:
+        out = torch.empty((n, H, DK), dtype=torch.float64, device=S.device)
+    st = load().qrs_channel_error(n, H, _dev(S, torch.float32, (n, H, DK, DV), "S"),
+                                  _opt(smooth, torch.float32, (H, DV), "smooth"),
+                                  _dev(out, torch.float64, (n, H, DK), "e"), _stream())
+    _check(st, "qrs_channel_error")
+    return out
+
+
+def persistence_window(a: torch.Tensor, sample_seq: torch.Tensor, sample_t: torch.Tensor,
+                       horizon: int = 256, out=None) -> torch.Tensor:
+    """qrs_persistence_window: W [n][H][128] (float64) from decays
+    a [n_seq][T][H][128] (float32) at the sampled writes (int32 [n] each)."""
+    n_seq, T, H = a.shape[0], a.shape[1], a.shape[2]
+    n = sample_seq.numel()
+    if out is None:
+        out = torch.empty((n, H, DK), dtype=torch.float64, device=a.device)
+    st = load().qrs_persistence_window(
+        n_seq, T, H, _dev(a, torch.float32, (n_seq, T, H, DK), "a"), n,
+        _dev(sample_seq, torch.int32, (n,), "sample_seq"),
+        _dev(sample_t, torch.int32, (n,), "sample_t"), int(horizon),
+        _dev(out, torch.float64, (n, H, DK), "W"), _stream())
+    _check(st, "qrs_persistence_window")
+    return out
+
+
+def persistence_geometric(a: torch.Tensor, sample_seq: torch.Tensor, sample_t: torch.Tensor,
+                          weight: torch.Tensor, tau: float = 1e-4, out=None) -> torch.Tensor:
+    """qrs_persistence_geometric: P [H][128] (float64)."""
+    n_seq, T, H = a.shape[0], a.shape[1], a.shape[2]
+    n = sample_seq.numel()
+    if out is None:
+        out = torch.empty((H, DK), dtype=torch.float64, device=a.device)
+    st = load().qrs_persistence_geometric(
+        n_seq, T, H, _dev(a, torch.float32, (n_seq, T, H, DK), "a"), n,
+        _dev(sample_seq, torch.int32, (n,), "sample_seq"),
+        _dev(sample_t, torch.int32, (n,), "sample_t"),
+        _dev(weight, torch.float64, (n,), "weight"), float(tau),
+        _dev(out, torch.float64, (H, DK), "P"), _stream())
+    _check(st, "qrs_persistence_geometric")
+    return out
+
+
+def channel_scores(e: torch.Tensor, weight: torch.Tensor, W: torch.Tensor | None = None,
+                   P: torch.Tensor | None = None, out=None) -> torch.Tensor:
+    """qrs_channel_scores: C [H][128] (float64); exactly one of W, P."""
+    n, H = e.shape[0], e.shape[1]
+    if out is None:
+        out = torch.empty((H, DK), dtype=torch.float64, device=e.device)
+    st = load().qrs_channel_scores(n, H, _dev(e, torch.float64, (n, H, DK), "e"),
+                                   _opt(W, torch.float64, (n, H, DK), "W"),
+                                   _opt(P, torch.float64, (H, DK), "P"),
+                                   _dev(weight, torch.float64, (n,), "weight"),
+                                   _dev(out, torch.float64, (H, DK), "C"), _stream())
+    _check(st, "qrs_channel_scores")
+    return out
+
+
+def select_protected_channels(score, k_hi: int = KHI) -> np.ndarray:
+    """qrs_select_protected_channels: perm int32 [H][128] (host) from scores
+    [H][128]; the first k_hi entries of each head are its protected channels."""
+    sc = np.ascontiguousarray(score.cpu().numpy() if isinstance(score, torch.Tensor) else score,
+                              dtype=np.float64)
+    H = sc.shape[0]
+    perm = np.empty((H, DK), np.int32)
+    st = load().qrs_select_protected_channels(H, sc.ctypes.data_as(ctypes.c_void_p), int(k_hi),
+                                              perm.ctypes.data_as(ctypes.c_void_p))
+    _check(st, "qrs_select_protected_channels")
+    return perm

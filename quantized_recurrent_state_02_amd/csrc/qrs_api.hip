@@ -5,6 +5,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <algorithm>
+#include <numeric>
 #include <vector>
 
 #include "../../include/qrs.h"
@@ -25,6 +27,18 @@ hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, i
                           int chunk, int in_bf16, const void *q, const void *k, const void *v,
                           const float *alpha, const float *beta, float *o, int init_from_pool,
                           hipStream_t stream);
+hipError_t launch_channel_error(int n, int num_heads, const float *S, const float *smooth,
+                                double *e, hipStream_t stream);
+hipError_t launch_persistence_window(int n_seq, int T, int num_heads, const float *a, int n,
+                                     const int32_t *sample_seq, const int32_t *sample_t,
+                                     int horizon, double *W, hipStream_t stream);
+hipError_t launch_persistence_geometric(int n_seq, int T, int num_heads, const float *a, int n,
+                                        const int32_t *sample_seq, const int32_t *sample_t,
+                                        const double *weight, double tau, double *P,
+                                        hipStream_t stream);
+hipError_t launch_channel_scores(int n, int num_heads, const double *e, const double *W,
+                                 const double *P, const double *weight, double *C,
+                                 hipStream_t stream);
 }  // namespace qrs
 
 struct qrs_pool_s {
@@ -250,6 +264,78 @@ int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int c
                                beta, o, init_from_pool, stream) == hipSuccess
                ? QRS_OK
                : QRS_EDEVICE;
+}
+
+int qrs_channel_error(int n, int num_heads, const float *S, const float *smooth, double *e,
+                      hipStream_t stream) {
+    if (n < 0 || num_heads < 1) return QRS_EINVAL;
+    if (n == 0) return QRS_OK;
+    if (!S || !e) return QRS_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(S) | reinterpret_cast<uintptr_t>(smooth)) % 16 != 0)
+        return QRS_EINVAL;
+    if ((size_t)n * (size_t)num_heads > 0x7fffffffu) return QRS_EINVAL;
+    return qrs::launch_channel_error(n, num_heads, S, smooth, e, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
+}
+
+int qrs_persistence_window(int n_seq, int T, int num_heads, const float *a, int n,
+                           const int32_t *sample_seq, const int32_t *sample_t, int horizon,
+                           double *W, hipStream_t stream) {
+    if (n < 0 || n_seq < 1 || T < 1 || num_heads < 1 || horizon < 0) return QRS_EINVAL;
+    if (n == 0) return QRS_OK;
+    if (!a || !sample_seq || !sample_t || !W) return QRS_EINVAL;
+    if ((size_t)n * (size_t)num_heads > 0x7fffffffu) return QRS_EINVAL;
+    return qrs::launch_persistence_window(n_seq, T, num_heads, a, n, sample_seq, sample_t, horizon,
+                                          W, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
+}
+
+int qrs_persistence_geometric(int n_seq, int T, int num_heads, const float *a, int n,
+                              const int32_t *sample_seq, const int32_t *sample_t,
+                              const double *weight, double tau, double *P, hipStream_t stream) {
+    if (n < 0 || n_seq < 1 || T < 1 || num_heads < 1 || !(tau > 0.0) || !std::isfinite(tau))
+        return QRS_EINVAL;
+    if (!P || (n > 0 && (!a || !sample_seq || !sample_t || !weight))) return QRS_EINVAL;
+    return qrs::launch_persistence_geometric(n_seq, T, num_heads, a, n, sample_seq, sample_t,
+                                             weight, tau, P, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
+}
+
+int qrs_channel_scores(int n, int num_heads, const double *e, const double *W, const double *P,
+                       const double *weight, double *C, hipStream_t stream) {
+    if (n < 0 || num_heads < 1 || (W == nullptr) == (P == nullptr) || !C) return QRS_EINVAL;
+    if (n > 0 && (!e || !weight)) return QRS_EINVAL;
+    return qrs::launch_channel_scores(n, num_heads, e, W, P, weight, C, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
+}
+
+int qrs_select_protected_channels(int num_heads, const double *score_host, int k_hi,
+                                  int32_t *perm_host) {
+    if (num_heads < 1 || k_hi < 0 || k_hi > qrs::DK || !score_host || !perm_host)
+        return QRS_EINVAL;
+    std::vector<int> order(qrs::DK);
+    std::vector<char> chosen(qrs::DK);
+    for (int h = 0; h < num_heads; ++h) {
+        const double *sc = score_host + (size_t)h * qrs::DK;
+        // a NaN score ranks below every number
+        auto key = [&](int u) { return std::isnan(sc[u]) ? -INFINITY : sc[u]; };
+        std::iota(order.begin(), order.end(), 0);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int x, int y) { return key(x) > key(y); });
+        std::fill(chosen.begin(), chosen.end(), 0);
+        for (int i = 0; i < k_hi; ++i) chosen[order[i]] = 1;
+        int32_t *pm = perm_host + (size_t)h * qrs::DK;
+        int pos = 0;
+        for (int u = 0; u < qrs::DK; ++u)
+            if (chosen[u]) pm[pos++] = u;
+        for (int u = 0; u < qrs::DK; ++u)
+            if (!chosen[u]) pm[pos++] = u;
+    }
+    return QRS_OK;
 }
 
 const char *qrs_status_string(int status) {

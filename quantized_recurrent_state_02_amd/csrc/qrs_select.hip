@@ -1,0 +1,179 @@
+// qrs_select.hip -- statistics for the offline choice of the FP16 key channels
+// (DAMP arXiv HTML, section 4 "Accumulated-error risk" and "Budgeted
+// selection", Appendix A.2 Eqs.(13)-(15); v2 reading notes, section 2.5).
+//
+//   channel_error_kernel      e[s][h][u]: squared error of key channel u of
+//                             calibration state s under the INT8 storage
+//                             mapping, in model coordinates (Eq.(14) integrand)
+//   persistence_window_kernel W[s][h][u] = 1 + sum_{j=1..H} prod_{r<=j} a_{t+r,u}^2
+//                             over the sample's own trajectory (v2 notes)
+//   persistence_geo_kernel    P[h][u] = 1 / max(1 - a_eff^2, tau),
+//                             a_eff = exp(sum_s w_s log a_s)  (Eq.(15))
+//   channel_scores_kernel     C[h][u] = sum_s w_s e_s W_s, or (sum_s w_s e_s) P
+//
+// The error kernel reads each 64 KiB calibration state once with 16-byte
+// loads (HBM-bound); the others are small.  Sums over samples run in sample
+// order inside one thread, so every result is deterministic.  Multiply-add
+// contraction is off in this file: each product and sum is rounded on its
+// own, in the order written.
+#include "qrs_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace qrs {
+
+namespace {
+
+constexpr int SEL_THREADS = 128;
+
+// One workgroup per (sample, head).  Thread t works on row 4 p + (t >> 5) in
+// pass p (32 passes) and holds columns 4 (t & 31) .. +3; the eight threads of
+// one 32-value group are consecutive lanes.
+__global__ __launch_bounds__(SEL_THREADS) void channel_error_kernel(
+    const float *__restrict__ S, const float *__restrict__ smooth, int num_heads,
+    double *__restrict__ e) {
+    const int tid = threadIdx.x;
+    const size_t sh = blockIdx.x;
+    const int h = (int)(sh % (size_t)num_heads);
+    const int rr = tid >> 5;
+    const int l = tid & 31;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(S + sh * (size_t)(DK * DV), DK * DV * 4);
+    float4 c4 = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (smooth) c4 = *reinterpret_cast<const float4 *>(smooth + (size_t)h * DV + 4 * l);
+    const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+    for (int p = 0; p < DK / 4; ++p) {
+        const int u = 4 * p + rr;
+        const U4 s4 = buf_load16(sr, (u * DV + 4 * l) * 4, 0);
+        const float sv[4] = {__builtin_bit_cast(float, s4.x), __builtin_bit_cast(float, s4.y),
+                             __builtin_bit_cast(float, s4.z), __builtin_bit_cast(float, s4.w)};
+        float x[4];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = sv[i] / cv[i];  // stored value coordinates, IEEE divide
+            amax = fmaxf(amax, fabsf(x[i]));
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        const float s = group_scale(amax);
+        const double rinv = scale_reciprocal(s);
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float code = fminf(fmaxf(rintf(quant_quotient(x[i], rinv)), -127.f), 127.f);
+            const float back = (s * code) * cv[i];
+            const double d = (double)back - (double)sv[i];
+            acc += d * d;
+        }
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) acc += __shfl_xor(acc, off, 64);
+        if (l == 0) e[sh * DK + u] = acc;
+    }
+}
+
+__device__ __forceinline__ bool sample_ok(int seq, int t, int n_seq, int T) {
+    return seq >= 0 && seq < n_seq && t >= 0 && t < T;
+}
+
+// One workgroup per (sample, head), thread u = key channel.
+__global__ __launch_bounds__(SEL_THREADS) void persistence_window_kernel(
+    const float *__restrict__ a, int n_seq, int T, int num_heads,
+    const int32_t *__restrict__ sample_seq, const int32_t *__restrict__ sample_t, int horizon,
+    double *__restrict__ W) {
+    const int u = threadIdx.x;
+    const size_t sh = blockIdx.x;
+    const size_t s = sh / (size_t)num_heads;
+    const int h = (int)(sh % (size_t)num_heads);
+    const int seq = sample_seq[s], t = sample_t[s];
+    double acc = __builtin_nan("");
+    if (sample_ok(seq, t, n_seq, T)) {
+        double p = 1.0;
+        acc = 1.0;
+        const int last = min(horizon, T - 1 - t);
+        for (int j = 1; j <= last; ++j) {
+            const double aj = (double)a[(((size_t)seq * T + (t + j)) * num_heads + h) * DK + u];
+            p = p * (aj * aj);
+            acc = acc + p;
+        }
+    }
+    W[sh * DK + u] = acc;
+}
+
+// One workgroup per head, thread u = key channel.
+__global__ __launch_bounds__(SEL_THREADS) void persistence_geo_kernel(
+    const float *__restrict__ a, int n_seq, int T, int num_heads, int n,
+    const int32_t *__restrict__ sample_seq, const int32_t *__restrict__ sample_t,
+    const double *__restrict__ weight, double tau, double *__restrict__ P) {
+    const int u = threadIdx.x;
+    const int h = blockIdx.x;
+    double L = 0.0;
+    for (int s = 0; s < n; ++s) {
+        const double w = weight[s];
+        if (w == 0.0) continue;
+        const int seq = sample_seq[s], t = sample_t[s];
+        if (!sample_ok(seq, t, n_seq, T)) {
+            L = __builtin_nan("");
+            break;
+        }
+        const double as = (double)a[(((size_t)seq * T + t) * num_heads + h) * DK + u];
+        L = L + w * log(as);
+    }
+    const double ae = exp(L);
+    const double gap = 1.0 - ae * ae;
+    // fmax would drop a NaN gap (an out-of-range sample); keep it
+    P[(size_t)h * DK + u] = gap != gap ? gap : 1.0 / fmax(gap, tau);
+}
+
+// One workgroup per head, thread u = key channel.
+__global__ __launch_bounds__(SEL_THREADS) void channel_scores_kernel(
+    int n, int num_heads, const double *__restrict__ e, const double *__restrict__ W,
+    const double *__restrict__ P, const double *__restrict__ weight, double *__restrict__ C) {
+    const int u = threadIdx.x;
+    const int h = blockIdx.x;
+    double acc = 0.0;
+    for (int s = 0; s < n; ++s) {
+        const size_t i = ((size_t)s * num_heads + h) * DK + u;
+        double term = weight[s] * e[i];
+        if (W) term = term * W[i];
+        acc = acc + term;
+    }
+    if (P) acc = acc * P[(size_t)h * DK + u];
+    C[(size_t)h * DK + u] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_channel_error(int n, int num_heads, const float *S, const float *smooth,
+                                double *e, hipStream_t stream) {
+    hipLaunchKernelGGL(channel_error_kernel, dim3((unsigned)(n * num_heads)), dim3(SEL_THREADS),
+                       0, stream, S, smooth, num_heads, e);
+    return hipGetLastError();
+}
+
+hipError_t launch_persistence_window(int n_seq, int T, int num_heads, const float *a, int n,
+                                     const int32_t *sample_seq, const int32_t *sample_t,
+                                     int horizon, double *W, hipStream_t stream) {
+    hipLaunchKernelGGL(persistence_window_kernel, dim3((unsigned)(n * num_heads)),
+                       dim3(SEL_THREADS), 0, stream, a, n_seq, T, num_heads, sample_seq, sample_t,
+                       horizon, W);
+    return hipGetLastError();
+}
+
+hipError_t launch_persistence_geometric(int n_seq, int T, int num_heads, const float *a, int n,
+                                        const int32_t *sample_seq, const int32_t *sample_t,
+                                        const double *weight, double tau, double *P,
+                                        hipStream_t stream) {
+    hipLaunchKernelGGL(persistence_geo_kernel, dim3((unsigned)num_heads), dim3(SEL_THREADS), 0,
+                       stream, a, n_seq, T, num_heads, n, sample_seq, sample_t, weight, tau, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_channel_scores(int n, int num_heads, const double *e, const double *W,
+                                 const double *P, const double *weight, double *C,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(channel_scores_kernel, dim3((unsigned)num_heads), dim3(SEL_THREADS), 0,
+                       stream, n, num_heads, e, W, P, weight, C);
+    return hipGetLastError();
+}
+
+}  // namespace qrs

@@ -109,3 +109,50 @@ def test_prefill_argument_validation(lib):
     for n, T, chunk, dt, init in ((-1, 8, 64, 0, 1), (1, -1, 64, 0, 1), (1, 8, 0, 0, 1),
                                   (1, 8, 65, 0, 1), (1, 8, 64, 2, 1), (1, 8, 64, 0, 2)):
         assert f(fake, p, n, T, chunk, dt, p, p, p, p, p, p, init, None) == -1
+
+
+def test_selection_argument_validation(lib):
+    """Host-side checks of the key-channel selection calls; every case is
+    rejected (or is an empty call) before anything is launched."""
+    p = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)   # not 16-byte aligned
+    f = lib.qrs_channel_error
+    assert f(-1, 4, p, None, p, None) == -1
+    assert f(1, 0, p, None, p, None) == -1
+    assert f(0, 4, None, None, None, None) == 0          # empty call
+    assert f(1, 4, None, None, p, None) == -1
+    assert f(1, 4, mis, None, p, None) == -1
+    assert f(1, 4, p, mis, p, None) == -1
+    w = lib.qrs_persistence_window
+    assert w(1, 8, 4, p, -1, p, p, 16, p, None) == -1
+    assert w(1, 8, 4, p, 2, p, p, -1, p, None) == -1
+    assert w(0, 8, 4, p, 2, p, p, 16, p, None) == -1
+    assert w(1, 8, 4, p, 0, None, None, 16, None, None) == 0
+    assert w(1, 8, 4, None, 2, p, p, 16, p, None) == -1
+    g = lib.qrs_persistence_geometric
+    for tau in (0.0, -1.0, float("nan"), float("inf")):
+        assert g(1, 8, 4, p, 2, p, p, p, tau, p, None) == -1
+    assert g(1, 8, 4, p, 2, p, p, p, 1e-4, None, None) == -1
+    assert g(1, 8, 4, None, 2, p, p, p, 1e-4, p, None) == -1
+    c = lib.qrs_channel_scores
+    assert c(2, 4, p, None, None, p, p, None) == -1       # neither W nor P
+    assert c(2, 4, p, p, p, p, p, None) == -1             # both
+    assert c(2, 4, p, p, None, p, None, None) == -1
+    s = lib.qrs_select_protected_channels
+    assert s(0, p, 16, p) == -1
+    assert s(1, p, 129, p) == -1
+    assert s(1, None, 16, p) == -1
+
+
+def test_select_protected_matches_oracle():
+    """The host selection against the oracle's Algorithm 1 on scores with
+    many ties, a NaN and several k_hi."""
+    from oracle import selector
+    r = np.random.default_rng(12)
+    score = r.integers(0, 30, (6, 128)).astype(np.float64)
+    score[2, 5] = np.nan
+    for k in (0, 1, 16, 127, 128):
+        perm = binding.select_protected_channels(score, k)
+        sc = np.where(np.isnan(score), -np.inf, score)
+        _, want = selector.select_protected(sc, k)
+        assert np.array_equal(perm, want), k
