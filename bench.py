@@ -247,7 +247,7 @@ def run_select(torch, binding, H, reps=3):
             "select_host_ms": t_sel * 1e3, "finite": ok}
 
 
-def cpu_select_baseline(H, samples=48):
+def cpu_select_baseline(H, samples=192):
     """The oracle's channel-error step on a bounded sample (samples x H states)."""
     from oracle import selector
 

@@ -41,33 +41,46 @@ __global__ __launch_bounds__(SEL_THREADS) void channel_error_kernel(
     float4 c4 = make_float4(1.f, 1.f, 1.f, 1.f);
     if (smooth) c4 = *reinterpret_cast<const float4 *>(smooth + (size_t)h * DV + 4 * l);
     const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-    for (int p = 0; p < DK / 4; ++p) {
-        const int u = 4 * p + rr;
-        const U4 s4 = buf_load16(sr, (u * DV + 4 * l) * 4, 0);
-        const float sv[4] = {__builtin_bit_cast(float, s4.x), __builtin_bit_cast(float, s4.y),
-                             __builtin_bit_cast(float, s4.z), __builtin_bit_cast(float, s4.w)};
-        float x[4];
-        float amax = 0.f;
+    // S / c as RN32(S * rc) with an FP64 reciprocal: the correctly rounded
+    // quotient, by the argument of quant_quotient (c > 0)
+    double rc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = sv[i] / cv[i];  // stored value coordinates, IEEE divide
-            amax = fmaxf(amax, fabsf(x[i]));
+    for (int j = 0; j < 4; ++j) rc[j] = scale_reciprocal(cv[j]);
+    // 16 rows per thread in flight: all loads of a batch are issued first
+    constexpr int BATCH = 16;
+    for (int p0 = 0; p0 < DK / 4; p0 += BATCH) {
+        U4 raw[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+            raw[i] = buf_load16(sr, ((4 * (p0 + i) + rr) * DV + 4 * l) * 4, 0);
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            const int u = 4 * (p0 + i) + rr;
+            const float sv[4] = {__builtin_bit_cast(float, raw[i].x), __builtin_bit_cast(float, raw[i].y),
+                                 __builtin_bit_cast(float, raw[i].z), __builtin_bit_cast(float, raw[i].w)};
+            float x[4];
+            float amax = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[j] = quant_quotient(sv[j], rc[j]);  // stored value coordinates
+                amax = fmaxf(amax, fabsf(x[j]));
+            }
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+            const float s = group_scale(amax);
+            const double rinv = scale_reciprocal(s);
+            double acc = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float code = fminf(fmaxf(rintf(quant_quotient(x[j], rinv)), -127.f), 127.f);
+                const float back = (s * code) * cv[j];
+                const double d = (double)back - (double)sv[j];
+                acc += d * d;
+            }
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) acc += __shfl_xor(acc, off, 64);
+            if (l == 0) e[sh * DK + u] = acc;
         }
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-        const float s = group_scale(amax);
-        const double rinv = scale_reciprocal(s);
-        double acc = 0.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float code = fminf(fmaxf(rintf(quant_quotient(x[i], rinv)), -127.f), 127.f);
-            const float back = (s * code) * cv[i];
-            const double d = (double)back - (double)sv[i];
-            acc += d * d;
-        }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) acc += __shfl_xor(acc, off, 64);
-        if (l == 0) e[sh * DK + u] = acc;
     }
 }
 
