@@ -59,6 +59,11 @@ def load():
     lib.orc_f64_decode.argtypes = [p, i, p, p, p, i, i, p, p, p, p, p, p]
     lib.orc_i8_prefill.argtypes = [p, p, p, i, p, p, p, i, i, i, p, p, p, p, p, p, i]
     lib.orc_channel_error.argtypes = [p, i, i, p, p]
+    lib.orc_hadamard32.argtypes = [p, p]
+    lib.orc_quantize_group_u8.argtypes = [p, p, p, p]
+    lib.orc_u8_store.argtypes = [p, p, p, i, p, p, p, i, p, i]
+    lib.orc_u8_dequant.argtypes = [p, p, p, i, p, p, p, i, p, i]
+    lib.orc_u8_decode.argtypes = [p, p, p, i, p, p, p, i, i, p, p, p, p, p, p]
     lib.orc_unit_bytes.argtypes = []
     lib.orc_unit_bytes.restype = i64
     _lib = lib
@@ -108,6 +113,31 @@ def quantize_group(x: np.ndarray):
     s = np.empty(1, dtype=np.float32)
     load().orc_quantize_group(_ptr(x), x.size, _ptr(code), _ptr(s))
     return code, s[0]
+
+
+def hadamard32(x: np.ndarray) -> np.ndarray:
+    """Normalized block-32 Hadamard transform of the last axis (length 32) of
+    x: y = H x / sqrt(32), H Sylvester order ([DAMP] HTML Appendix A.1,
+    Table 3).  FP64 sums in index order, times RN64(2^-2.5), rounded to FP32."""
+    x = _f32(x)
+    flat = x.reshape(-1, GRP)
+    out = np.empty_like(flat)
+    lib = load()
+    for r in range(flat.shape[0]):
+        lib.orc_hadamard32(_ptr(flat[r]), _ptr(out[r]))
+    return out.reshape(x.shape)
+
+
+def quantize_group_u8(y: np.ndarray):
+    """Asymmetric UINT8 codes of one transformed 32-value group with FP16
+    scale and zero point (HTML section 3.2 Eq.(3), Appendix A.1).  Returns
+    (codes uint8 [32], s16, z16) with s16, z16 the FP16 bit patterns."""
+    y = _f32(y).ravel()
+    assert y.size == GRP
+    code = np.empty(GRP, dtype=np.uint8)
+    sz = np.zeros(2, dtype=np.uint16)
+    load().orc_quantize_group_u8(_ptr(y), _ptr(code), _ptr(sz[0:1]), _ptr(sz[1:2]))
+    return code, sz[0], sz[1]
 
 
 def unit_bytes() -> int:
@@ -220,4 +250,47 @@ class OracleDensePool:
         fn = load().orc_f64_decode if self.dtype == np.float64 else load().orc_f32_decode
         fn(_ptr(self.T), self.num_heads, _ptr(self.perm), _ptr(self.c), _ptr(slots),
            slots.size, kind, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(o))
+        return o
+
+
+class OracleU8Pool:
+    """Packed pool with the first revision's low tier: stored key rows 0..15
+    as FP16 bits (``hi``), rows 16..127 as UINT8 codes of the normalized
+    block-32 Hadamard transform of each 32-value group (``lo``) with an FP16
+    scale and zero point per group (``meta`` [U][112][4][2]: s, z) -- the
+    INT8+Hadamard format of [DAMP] HTML section 3.2 Eq.(3), Appendix A.1
+    (Table 3) in the packed layout of Appendix A.5 Eq.(17).  Same
+    coordinates, permutation and smoothing as OraclePool."""
+
+    def __init__(self, num_slots, num_heads, perm=None, c=None):
+        self.num_slots = num_slots
+        self.num_heads = num_heads
+        U = num_slots * num_heads
+        self.hi = np.zeros((U, KHI, DV), dtype=np.uint16)
+        self.lo = np.zeros((U, KLO, DV), dtype=np.uint8)
+        self.meta = np.zeros((U, KLO, NGRP, 2), dtype=np.uint16)
+        self.perm = _i32(perm if perm is not None else np.tile(np.arange(DK), (num_heads, 1)))
+        self.c = _f32(c if c is not None else np.ones((num_heads, DV)))
+
+    def store(self, slots, S, space=0):
+        slots = _i32(slots)
+        S = _f32(S)
+        load().orc_u8_store(_ptr(self.hi), _ptr(self.lo), _ptr(self.meta), self.num_heads,
+                            _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, _ptr(S), space)
+
+    def dequant(self, slots, space=0):
+        slots = _i32(slots)
+        out = np.empty((slots.size, self.num_heads, DK, DV), dtype=np.float32)
+        load().orc_u8_dequant(_ptr(self.hi), _ptr(self.lo), _ptr(self.meta), self.num_heads,
+                              _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, _ptr(out),
+                              space)
+        return out
+
+    def decode_step(self, slots, q, k, v, gate, beta, kind):
+        slots = _i32(slots)
+        q, k, v, gate, beta = (_f32(a) for a in (q, k, v, gate, beta))
+        o = np.empty((slots.size, self.num_heads, DV), dtype=np.float32)
+        load().orc_u8_decode(_ptr(self.hi), _ptr(self.lo), _ptr(self.meta), self.num_heads,
+                             _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, kind,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(o))
         return o

@@ -447,6 +447,170 @@ void orc_i8_prefill(uint16_t *hi, int8_t *lo, float *sc, int num_heads, const in
 
 /* Sizes of the oracle's representation of one unit, in bytes. */
 /* ------------------------------------------------------------------ */
+/* The first revision's low tier ([DAMP] section 3.2 Eq.(3); Appendix   */
+/* A.1 and Table 3, "INT8+Hadamard"; Appendix A.5 Eq.(17)): a normalized */
+/* block-32 Hadamard transform along d_v, then asymmetric UINT8 codes    */
+/* with an FP16 scale and zero point per 32 values.  Same unit size as   */
+/* the INT8 tier above (4 bytes of metadata per group).                  */
+/* ------------------------------------------------------------------ */
+
+/* Normalized block-32 Hadamard, y = H x / sqrt(32) with H[i][j] =
+ * (-1)^popcount(i & j) (Sylvester order).  Each output is the FP64 sum over
+ * j in increasing order, times RN64(2^-2.5), rounded once to FP32.  The
+ * transform is its own inverse. */
+void orc_hadamard32(const float *x, float *y)
+{
+    const double inv = 1.0 / sqrt(32.0);
+    for (int i = 0; i < GRP; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < GRP; ++j) {
+            const int neg = __builtin_popcount((unsigned)(i & j)) & 1;
+            acc += neg ? -(double)x[j] : (double)x[j];
+        }
+        y[i] = (float)(acc * inv);
+    }
+}
+
+/* Eq.(3) with b = 8 on one transformed group y[32]:
+ *   s = (y_max - y_min) / 255, stored as FP16 s16 (round to nearest even);
+ *   z = round(-y_min / s16), stored as FP16 z16;
+ *   q_i = round(y_i / s16) + z16, saturated to [0, 255];
+ *   reconstruction y_hat_i = s16 (q_i - z16).
+ * Quantization uses the stored FP16 values, so codes and reconstruction
+ * agree.  All arithmetic FP32 (correctly rounded divides, round half to
+ * even).  A group whose stored scale is zero (constant group, or a scale
+ * below the FP16 range) stores s16 = z16 = 0 and codes 0. */
+void orc_quantize_group_u8(const float *y, uint8_t *q, uint16_t *s16, uint16_t *z16)
+{
+    float lo = y[0], hi = y[0];
+    for (int j = 1; j < GRP; ++j) {
+        if (y[j] < lo)
+            lo = y[j];
+        if (y[j] > hi)
+            hi = y[j];
+    }
+    const float s = (hi - lo) / 255.0f;
+    const uint16_t sb = orc_f32_to_f16(s);
+    const float sh = orc_f16_to_f32(sb);
+    if (sh == 0.0f) {
+        *s16 = 0;
+        *z16 = 0;
+        for (int j = 0; j < GRP; ++j)
+            q[j] = 0;
+        return;
+    }
+    const uint16_t zb = orc_f32_to_f16(rintf(-lo / sh));
+    const float zh = orc_f16_to_f32(zb);
+    for (int j = 0; j < GRP; ++j) {
+        float c = rintf(y[j] / sh) + zh;
+        if (c < 0.0f)
+            c = 0.0f;
+        if (c > 255.0f)
+            c = 255.0f;
+        q[j] = (uint8_t)c;
+    }
+    *s16 = sb;
+    *z16 = zb;
+}
+
+static void store_unit_u8(const float *T, uint16_t *hi, uint8_t *lo, uint16_t *meta)
+{
+    for (int i = 0; i < KHI; ++i)
+        for (int j = 0; j < DV; ++j)
+            hi[i * DV + j] = orc_f32_to_f16(T[i * DV + j]);
+    for (int i = KHI; i < DK; ++i)
+        for (int g = 0; g < NGRP; ++g) {
+            float y[GRP];
+            orc_hadamard32(&T[i * DV + g * GRP], y);
+            uint16_t *m = meta + ((i - KHI) * NGRP + g) * 2;
+            orc_quantize_group_u8(y, &lo[(i - KHI) * DV + g * GRP], &m[0], &m[1]);
+        }
+}
+
+static void dequant_unit_u8(const uint16_t *hi, const uint8_t *lo, const uint16_t *meta, float *T)
+{
+    for (int i = 0; i < KHI; ++i)
+        for (int j = 0; j < DV; ++j)
+            T[i * DV + j] = orc_f16_to_f32(hi[i * DV + j]);
+    for (int i = KHI; i < DK; ++i)
+        for (int g = 0; g < NGRP; ++g) {
+            const uint16_t *m = meta + ((i - KHI) * NGRP + g) * 2;
+            const float sh = orc_f16_to_f32(m[0]), zh = orc_f16_to_f32(m[1]);
+            float yh[GRP];
+            for (int j = 0; j < GRP; ++j)
+                yh[j] = sh * ((float)lo[(i - KHI) * DV + g * GRP + j] - zh);
+            orc_hadamard32(yh, &T[i * DV + g * GRP]);
+        }
+}
+
+/* Pool-level calls of the v1 tier; arrays as for the INT8 tier except
+ * lo [U][112][128] uint8 and meta [U][112][4][2] uint16 (FP16 s, z). */
+void orc_u8_store(uint16_t *hi, uint8_t *lo, uint16_t *meta, int num_heads, const int32_t *perm,
+                  const float *c, const int32_t *slots, int n, const float *S, int space)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t uu = 0; uu < (int64_t)n * num_heads; ++uu) {
+        int b = (int)(uu / num_heads), h = (int)(uu % num_heads);
+        int64_t u = (int64_t)slots[b] * num_heads + h;
+        const float *Sm = S + uu * DK * DV;
+        float *T = (float *)malloc(sizeof(float) * DK * DV);
+        for (int i = 0; i < DK; ++i)
+            for (int j = 0; j < DV; ++j)
+                T[i * DV + j] = space ? Sm[i * DV + j]
+                                      : Sm[perm[h * DK + i] * DV + j] / c[h * DV + j];
+        store_unit_u8(T, hi + u * KHI * DV, lo + u * KLO * DV, meta + u * KLO * NGRP * 2);
+        free(T);
+    }
+}
+
+void orc_u8_dequant(const uint16_t *hi, const uint8_t *lo, const uint16_t *meta, int num_heads,
+                    const int32_t *perm, const float *c, const int32_t *slots, int n, float *S,
+                    int space)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t uu = 0; uu < (int64_t)n * num_heads; ++uu) {
+        int b = (int)(uu / num_heads), h = (int)(uu % num_heads);
+        int64_t u = (int64_t)slots[b] * num_heads + h;
+        float *Sm = S + uu * DK * DV;
+        float *T = (float *)malloc(sizeof(float) * DK * DV);
+        dequant_unit_u8(hi + u * KHI * DV, lo + u * KLO * DV, meta + u * KLO * NGRP * 2, T);
+        for (int i = 0; i < DK; ++i)
+            for (int j = 0; j < DV; ++j) {
+                if (space)
+                    Sm[i * DV + j] = T[i * DV + j];
+                else
+                    Sm[perm[h * DK + i] * DV + j] = T[i * DV + j] * c[h * DV + j];
+            }
+        free(T);
+    }
+}
+
+/* The same compressed decode step with the v1 tier. */
+void orc_u8_decode(uint16_t *hi, uint8_t *lo, uint16_t *meta, int num_heads, const int32_t *perm,
+                   const float *c, const int32_t *slots, int n, int kind, const float *q,
+                   const float *k, const float *v, const float *gate, const float *beta,
+                   float *o /*[n][H][DV]*/)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t uu = 0; uu < (int64_t)n * num_heads; ++uu) {
+        int b = (int)(uu / num_heads), h = (int)(uu % num_heads);
+        int64_t u = (int64_t)slots[b] * num_heads + h;
+        float qp[DK], kp[DK], vp[DV], lam[DK];
+        gather_operands(kind, b, h, num_heads, perm, c, q, k, v, gate, qp, kp, vp, lam);
+        float *Th = (float *)malloc(sizeof(float) * DK * DV);
+        float *T = (float *)malloc(sizeof(float) * DK * DV);
+        uint16_t *uhi = hi + u * KHI * DV;
+        uint8_t *ulo = lo + u * KLO * DV;
+        uint16_t *umeta = meta + u * KLO * NGRP * 2;
+        dequant_unit_u8(uhi, ulo, umeta, Th);
+        step_unit_f32(Th, T, lam, kp, qp, vp, beta[uu], c + h * DV, o + uu * DV);
+        store_unit_u8(T, uhi, ulo, umeta);
+        free(Th);
+        free(T);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Key-channel selection: quantization-error energy of each key channel */
 /* ([DAMP] section 4 "Accumulated-error risk", Eq.(8), and Appendix A.2 */
 /* Eq.(14); [DAMP2] section 2.5, e_{t,u}).                              */

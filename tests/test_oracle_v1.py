@@ -1,0 +1,153 @@
+"""Pins of the oracle's v1 low tier: normalized block-32 Hadamard transform
+and asymmetric UINT8 codes with FP16 scale and zero point (DAMP arXiv HTML,
+section 3.2 Eq.(3); Appendix A.1 and Table 3 "INT8+Hadamard"; Appendix A.5
+Eq.(17)).
+"""
+import json
+import os
+
+import numpy as np
+from scipy.linalg import hadamard
+
+import oracle
+
+DK = DV = 128
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_hadamard_is_the_library_matrix():
+    """The transform equals Sylvester's H_32 (scipy) / sqrt(32) evaluated in
+    FP64 and rounded once, on groups whose values make every FP64 sum exact."""
+    r = np.random.default_rng(1)
+    H = hadamard(32).astype(np.float64) / np.sqrt(32.0)
+    for _ in range(200):
+        x = (r.normal(0, 1, 32) * np.exp(r.uniform(-5, 5))).astype(np.float32)
+        want = (hadamard(32).astype(np.float64) @ x.astype(np.float64)) * (1 / np.sqrt(32.0))
+        assert np.array_equal(oracle.hadamard32(x), want.astype(np.float32))
+        assert np.allclose(oracle.hadamard32(x), H @ x, rtol=1e-6, atol=1e-6 * np.abs(x).max())
+
+
+def test_hadamard_special_vectors_and_involution():
+    e0 = np.zeros(32, np.float32)
+    e0[0] = 1
+    assert np.all(oracle.hadamard32(e0) == np.float32(2.0 ** -2.5))
+    ones = np.ones(32, np.float32)
+    y = oracle.hadamard32(ones)
+    assert y[0] == np.float32(2.0 ** 2.5) and np.all(y[1:] == 0)
+    x = np.random.default_rng(2).normal(0, 1, (50, 32)).astype(np.float32)
+    back = oracle.hadamard32(oracle.hadamard32(x))
+    assert np.abs(back - x).max() <= 4e-7 * np.abs(x).max()
+    # orthonormal: energy preserved
+    yx = oracle.hadamard32(x).astype(np.float64)
+    assert np.allclose((yx ** 2).sum(1), (x.astype(np.float64) ** 2).sum(1), rtol=1e-6)
+
+
+def test_affine_codes_on_an_exact_grid():
+    """Eq.(3) where every quantity is exact: max - min = 255 * 2^-7, so
+    s = 2^-7 in FP16, z = 100, grid points get their index and half-way
+    points round to even."""
+    step = 2.0 ** -7
+    y = (-100 + np.arange(32) * 8.0) * step
+    y[31] = (-100 + 255) * step
+    y[5] = (-100 + 40.5) * step             # half-way between codes 40 and 41 -> 40 (even)
+    y[6] = (-100 + 41.5) * step             # -> 42 (even)
+    codes, s16, z16 = oracle.quantize_group_u8(y.astype(np.float32))
+    assert oracle.f16_bits_to_f32(np.array([s16]))[0] == np.float32(step)
+    assert oracle.f16_bits_to_f32(np.array([z16]))[0] == 100
+    want = np.arange(32) * 8
+    want[31], want[5], want[6] = 255, 40, 42
+    assert np.array_equal(codes, want.astype(np.uint8))
+
+
+def test_affine_codes_nearest_and_bounded():
+    """Random groups: codes are the nearest grid point s16 (c - z16) to each
+    value, checked by brute force over all 256 codes; the minimum maps to
+    code 0; reconstruction error at most s16/2 (plus the saturation slack
+    255 |s - s16| at the top)."""
+    r = np.random.default_rng(3)
+    for _ in range(300):
+        y = (r.normal(0, 1, 32) * np.exp(r.uniform(-3, 3)) + r.normal(0, 0.5)).astype(np.float32)
+        codes, s16, z16 = oracle.quantize_group_u8(y)
+        sh, zh = (float(v) for v in oracle.f16_bits_to_f32(np.array([s16, z16])))
+        grid = sh * (np.arange(256, dtype=np.float64) - zh)
+        lo, hi = float(y.min()), float(y.max())
+        s = float(np.float32(np.float32(hi - lo) / np.float32(255)))
+        if abs(zh) <= 2048:
+            assert codes[np.argmin(y)] == 0
+        for j in range(32):
+            err = abs(grid[codes[j]] - float(y[j]))
+            assert err <= sh / 2 * (1 + 1e-6) + 255 * abs(s - sh) + 1e-12, (j, err, sh)
+            best = np.min(np.abs(grid - float(y[j])))
+            assert err <= best + 1e-6 * sh
+
+
+def test_constant_group():
+    codes, s16, z16 = oracle.quantize_group_u8(np.full(32, 0.75, np.float32))
+    assert s16 == 0 and z16 == 0 and not codes.any()
+
+
+def test_storage_bits_of_the_v1_tier():
+    """Table 3: INT8+Hadamard stores 8 bits per value plus FP16 s and z per 32
+    values = 9.0 bits; with 16 FP16 rows the unit has the same 20,224 bytes
+    as the INT8 tier (Eq.(12))."""
+    golden = json.load(open(os.path.join(GOLDEN, "storage_bits.json")))
+    per_group_bits = 32 * 8 + 2 * 16
+    assert per_group_bits / 32 == golden["int8_hadamard_fp16_sz_bits"]
+    unit = 16 * DV * 2 + 112 * DV * 1 + 112 * (DV // 32) * 4
+    assert unit == 20224
+    assert unit * 8 / (DK * DV) == golden["bits_per_value"]
+
+
+def test_pool_round_trip_preserves_energy():
+    """store -> dequant: the squared error of each 32-value group in stored
+    coordinates equals its error in the transformed domain (the transform
+    is orthonormal), and stays within the quantization step."""
+    r = np.random.default_rng(4)
+    H = 2
+    S = r.normal(0, 0.1, (1, H, DK, DV)).astype(np.float32)
+    S[0, :, 20, :] *= 20
+    pool = oracle.OracleU8Pool(1, H)
+    pool.store([0], S, space=1)
+    T = pool.dequant([0], space=1)[0]
+    for h in range(H):
+        for i in (16, 20, 77, 127):
+            for g in range(4):
+                x = S[0, h, i, 32 * g:32 * g + 32]
+                y = oracle.hadamard32(x).astype(np.float64)
+                sh, zh = oracle.f16_bits_to_f32(pool.meta[h, i - 16, g])
+                yh = float(sh) * (pool.lo[h, i - 16, 32 * g:32 * g + 32].astype(np.float64) - float(zh))
+                ex = ((T[h, i, 32 * g:32 * g + 32].astype(np.float64) - x) ** 2).sum()
+                ey = ((np.float32(yh).astype(np.float64) - y) ** 2).sum()
+                assert abs(ex - ey) <= 1e-4 * ey + 1e-12
+                assert ey <= 32 * (float(sh) / 2) ** 2 * 1.01
+        # FP16 rows are the FP16 rounding of the input
+        assert np.array_equal(T[h, :16], S[0, h, :16].astype(np.float16).astype(np.float32))
+
+
+def test_decode_step_composes_codec_and_fp32_step():
+    """One v1 decode step equals dequant -> the FP32 step of the
+    uncompressed oracle (same coordinates) -> store."""
+    r = np.random.default_rng(5)
+    H, n = 2, 2
+    perm = np.stack([r.permutation(DK) for _ in range(H)]).astype(np.int32)
+    c = np.exp(r.uniform(-0.69, 0.69, (H, DV))).astype(np.float32)
+    S = r.normal(0, 0.1, (n, H, DK, DV)).astype(np.float32)
+    pool = oracle.OracleU8Pool(n, H, perm, c)
+    slots = np.arange(n, dtype=np.int32)
+    pool.store(slots, S)
+    T0 = pool.dequant(slots, space=1)
+    q = r.normal(0, 1, (n, H, DK)).astype(np.float32)
+    k = r.normal(0, 1, (n, H, DK)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.normal(0, 1, (n, H, DV)).astype(np.float32)
+    g = (-np.abs(r.normal(0, 1, (n, H, DK)))).astype(np.float32)
+    beta = r.uniform(0, 1, (n, H)).astype(np.float32)
+    o = pool.decode_step(slots, q, k, v, g, beta, 1)
+    dense = oracle.OracleDensePool(n, H, perm, c)
+    dense.T[:] = T0.reshape(n * H, DK, DV)
+    o2 = dense.decode_step(slots, q, k, v, g, beta, 1)
+    assert np.array_equal(o, o2)
+    ref = oracle.OracleU8Pool(n, H, perm, c)
+    ref.store(slots, dense.T.reshape(n, H, DK, DV), space=1)
+    assert np.array_equal(pool.lo, ref.lo) and np.array_equal(pool.meta, ref.meta)
+    assert np.array_equal(pool.hi, ref.hi)
