@@ -456,11 +456,12 @@ void orc_i8_prefill(uint16_t *hi, int8_t *lo, float *sc, int num_heads, const in
 
 /* Normalized block-32 Hadamard, y = H x / sqrt(32) with H[i][j] =
  * (-1)^popcount(i & j) (Sylvester order).  Each output is the FP64 sum over
- * j in increasing order, times RN64(2^-2.5), rounded once to FP32.  The
- * transform is its own inverse. */
+ * j in increasing order, times RN64(2^-2.5) (= RN64(sqrt 2) / 8, the
+ * correctly rounded 1/sqrt(32)), rounded once to FP32.  The transform is its
+ * own inverse. */
 void orc_hadamard32(const float *x, float *y)
 {
-    const double inv = 1.0 / sqrt(32.0);
+    const double inv = sqrt(2.0) * 0.125;
     for (int i = 0; i < GRP; ++i) {
         double acc = 0.0;
         for (int j = 0; j < GRP; ++j) {

@@ -16,13 +16,14 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def test_hadamard_is_the_library_matrix():
-    """The transform equals Sylvester's H_32 (scipy) / sqrt(32) evaluated in
-    FP64 and rounded once, on groups whose values make every FP64 sum exact."""
+    """The transform equals Sylvester's H_32 (scipy) times the correctly
+    rounded 2^-2.5 = 1/sqrt(32) in FP64, rounded once, on groups whose values
+    make every FP64 sum exact."""
     r = np.random.default_rng(1)
     H = hadamard(32).astype(np.float64) / np.sqrt(32.0)
     for _ in range(200):
         x = (r.normal(0, 1, 32) * np.exp(r.uniform(-5, 5))).astype(np.float32)
-        want = (hadamard(32).astype(np.float64) @ x.astype(np.float64)) * (1 / np.sqrt(32.0))
+        want = (hadamard(32).astype(np.float64) @ x.astype(np.float64)) * (np.sqrt(2.0) / 8)
         assert np.array_equal(oracle.hadamard32(x), want.astype(np.float32))
         assert np.allclose(oracle.hadamard32(x), H @ x, rtol=1e-6, atol=1e-6 * np.abs(x).max())
 
