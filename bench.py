@@ -26,7 +26,10 @@ timed on a bounded sample of the same workload.
 `detail` also reports KDA decode, the single-pool variants, the FP32-state
 kernel on the same inputs, and the chunked prefill kernel (8 x 32 heads x
 4096 tokens, chunks of 64, FP32 and bf16 q/k/v) against the FP32 matrix-core
-peak, and the key-channel selection kernels on a calibration-shaped sample.
+peak, the key-channel selection kernels on a calibration-shaped sample, and
+the first revision's low tier (block-32 Hadamard + UINT8 with FP16 scale and
+zero point) on the decode workload, with its trajectory error next to the
+INT8 tier's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -194,6 +197,41 @@ def run_prefill(torch, binding, inputs, bf16, reps=3):
                               f"{'bf16' if bf16 else 'fp32'} q/k/v, zero initial state"}
 
 
+def run_codec_compare(torch, binding, inputs, dev_in, perm, c, n, H, steps):
+    """GDN at the serving shape, the INT8 tier and the first revision's tier
+    (block-32 Hadamard + UINT8, FP16 s and z) against the uncompressed FP32
+    recurrence on identical inputs: RRMSE of every step's readout and of the
+    final state (model coordinates)."""
+    S0 = torch.from_numpy(inputs.initial_state(1, n, H)).to("cuda")
+    slots = torch.arange(n, dtype=torch.int32, device="cuda")
+    pools = {name: binding.StatePool(fmt, n, H, perm, c)
+             for name, fmt in (("int8", binding.FMT_I8F16), ("u8_hadamard", binding.FMT_U8H16),
+                               ("fp32", binding.FMT_FP32))}
+    for p in pools.values():
+        p.store(slots, S0)
+    outs = {name: torch.empty((n, H, 128), device="cuda") for name in pools}
+    num = {name: torch.zeros((), dtype=torch.float64, device="cuda") for name in ("int8", "u8_hadamard")}
+    den = torch.zeros((), dtype=torch.float64, device="cuda")
+    for t in range(steps):
+        for name, p in pools.items():
+            p.gdn_step(slots, dev_in["q"][t], dev_in["k"][t], dev_in["v"][t], dev_in["alpha"][t],
+                       dev_in["beta"][t], outs[name])
+        ref = outs["fp32"].double()
+        for name in num:
+            num[name] += ((outs[name].double() - ref) ** 2).sum()
+        den += (ref ** 2).sum()
+    Sref = pools["fp32"].dequant(slots).double()
+    res = {"workload": f"GDN, {n} slots x {H} heads, {steps} steps from the same stored start"}
+    for name in num:
+        Sq = pools[name].dequant(slots).double()
+        res[name] = {"readout_rrmse": float(torch.sqrt(num[name] / den)),
+                     "final_state_rrmse": float(torch.sqrt(((Sq - Sref) ** 2).sum() / (Sref ** 2).sum()))}
+    for p in pools.values():
+        p.close()
+    torch.cuda.empty_cache()
+    return res
+
+
 # Key-channel selection, calibration-shaped: 32 sequences of 256 steps, 32
 # heads, one sampled state every 8 steps (1,024 samples per head).  The error
 # kernel reads every sampled FP32 state once (64 KiB per sample and head).
@@ -313,7 +351,7 @@ def main():
                     help="slot sets rotated per step (4 = cache-cold working set)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gdn", "kda", "f32", "prefill", "select", "all"],
+    ap.add_argument("--only", choices=["gdn", "kda", "f32", "v1", "prefill", "select", "all"],
                     default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
@@ -351,7 +389,8 @@ def main():
 
     perm1 = inputs.protected_perm(1, H)
     c1 = inputs.smoothing(1, H, True)
-    if args.only in ("gdn", "f32", "all"):
+    codec_cmp = None
+    if args.only in ("gdn", "f32", "v1", "all"):
         gdn_in = stage_inputs(torch, inputs, 1, "gdn", n, H, total)
         if args.only in ("gdn", "all"):
             for pools in sorted({args.pools, 1}, reverse=True):
@@ -364,6 +403,14 @@ def main():
                                   c1, n, H, steps, warmup, 1, use_graph)
             res[("f32", 1)] = (secs, ok)
             log(f"[bench] fp32-state gdn: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        if args.only in ("v1", "all"):
+            secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_U8H16, gdn_in, perm1,
+                                  c1, n, H, steps, warmup, args.pools, use_graph)
+            res[("gdnv1", args.pools)] = (secs, ok)
+            log(f"[bench] gdn u8+hadamard pools={args.pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+            codec_cmp = run_codec_compare(torch, binding, inputs, gdn_in, perm1, c1, n, H,
+                                          min(256, total))
+            log(f"[bench] codec comparison: {codec_cmp}")
         del gdn_in
         torch.cuda.empty_cache()
     if args.only in ("kda", "all"):
@@ -429,11 +476,12 @@ def main():
     out = {}
     head_key = ("gdn", args.pools) if ("gdn", args.pools) in res else next(iter(res))
     kind0 = head_key[0]
-    nbytes0 = {"gdn": BYTES_GDN, "kda": BYTES_KDA, "f32": BYTES_F32_GDN}[kind0]
+    NB = {"gdn": BYTES_GDN, "gdnv1": BYTES_GDN, "kda": BYTES_KDA, "f32": BYTES_F32_GDN}
+    nbytes0 = NB[kind0]
     head = rate(head_key, nbytes0)
     detail = {}
     for key in res:
-        nb = {"gdn": BYTES_GDN, "kda": BYTES_KDA, "f32": BYTES_F32_GDN}[key[0]]
+        nb = NB[key[0]]
         detail[f"{key[0]}_pools{key[1]}"] = rate(key, nb)
     if ("gdn", 1) in res and ("f32", 1) in res:
         detail["speedup_vs_fp32_state"] = res[("f32", 1)][0] / res[("gdn", 1)][0]
@@ -441,6 +489,8 @@ def main():
         detail["prefill"] = prefill
     if select:
         detail["select"] = select
+    if codec_cmp:
+        detail["codec_comparison"] = codec_cmp
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -461,8 +511,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{kind0}_decode_compressed_state" if kind0 != "f32"
-                   else "gdn_decode_fp32_state",
+        "config": {"workload": {"gdn": "gdn_decode_compressed_state",
+                                "kda": "kda_decode_compressed_state",
+                                "gdnv1": "gdn_decode_u8_hadamard_state",
+                                "f32": "gdn_decode_fp32_state"}[kind0],
                    "batch": n, "heads": H, "d_k": 128, "d_v": 128,
                    "state_format": "16 FP16 + 112 INT8 key rows, FP32 absmax/127 scale per 32",
                    "slot_sets_rotated": args.pools if kind0 != "f32" else 1,

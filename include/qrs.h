@@ -34,7 +34,8 @@
  *    it).  QRS_EINVAL: null pointer, negative size, bad enum, a perm that is
  *    not a permutation, a non-positive or non-finite smoothing scale, a buffer
  *    too small.  QRS_EUNSUPPORTED: a shape other than d_k = d_v = 128,
- *    k_hi = 16, group = 32 (FP32 pools: k_hi = group = 0).  QRS_EDEVICE: a HIP
+ *    k_hi = 16, group = 32 (FP32 pools: k_hi = group = 0), or a call a pool
+ *    format does not support.  QRS_EDEVICE: a HIP
  *    launch or copy failed (asynchronous faults surface at the caller's next
  *    synchronization).  Nothing is enqueued when the call returns an error.
  *  - Slot ids: int32 device array of length n.  Ids must be distinct within
@@ -61,7 +62,9 @@ typedef struct qrs_pool_s *qrs_pool;
 /* Pool formats. */
 enum {
     QRS_FMT_FP32 = 0,  /* uncompressed FP32 state (compression disabled) */
-    QRS_FMT_I8F16 = 1  /* 16 FP16 rows + 112 INT8 rows, FP32 scale per 32 values */
+    QRS_FMT_I8F16 = 1, /* 16 FP16 rows + 112 INT8 rows, FP32 scale per 32 values */
+    QRS_FMT_U8H16 = 2  /* 16 FP16 rows + 112 UINT8 rows of the block-32 Hadamard transform,
+                          FP16 scale and zero point per 32 values (the first revision's tier) */
 };
 
 /* Coordinate spaces for store / dequant. */
@@ -77,6 +80,20 @@ enum {
     QRS_EUNSUPPORTED = -2,
     QRS_EDEVICE = -3
 };
+
+/*
+ * QRS_FMT_U8H16 ([DAMP] HTML section 3.2 Eq.(3); Appendix A.1, Table 3
+ * "INT8+Hadamard"; Appendix A.5 Eq.(17)): each 32-value group x of an
+ * INT8-tier row is transformed, y = H_32 x / sqrt(32) (Sylvester order; FP64
+ * sums, times RN64(2^-2.5), rounded once to FP32), then coded as
+ *   s = RN32((max y - min y) / 255) -> FP16 s16;  z = round(-min y / s16) -> FP16 z16;
+ *   code = min(max(round(y / s16) + z16, 0), 255)   (round half to even),
+ * and read back as x = H_32 (s16 (code - z16)) / sqrt(32).  A zero s16
+ * stores s16 = z16 = 0 and codes 0.  Same unit size and offsets as
+ * QRS_FMT_I8F16; the 4-byte word of a group holds s16 in bits 0..15 and z16
+ * in bits 16..31.  Decode and store/dequant support it; chunked prefill
+ * returns QRS_EUNSUPPORTED.
+ */
 
 /*
  * Layout of one unit u = slot * num_heads + head, at byte offset

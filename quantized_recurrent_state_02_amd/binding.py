@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libqrs.so")
 
 FMT_FP32 = 0
 FMT_I8F16 = 1
+FMT_U8H16 = 2
 SPACE_MODEL = 0
 SPACE_STORED = 1
 OK = 0
 DK = DV = 128
 KHI = 16
 GRP = 32
-UNIT_BYTES = {FMT_FP32: 65536, FMT_I8F16: 20224}
+UNIT_BYTES = {FMT_FP32: 65536, FMT_I8F16: 20224, FMT_U8H16: 20224}
 HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
 
 EXPORTED = (
@@ -110,7 +111,7 @@ def _dev(t: torch.Tensor, dtype, shape, name):
 
 
 def pool_bytes(fmt: int, num_slots: int, num_heads: int) -> int:
-    khi, grp = (KHI, GRP) if fmt == FMT_I8F16 else (0, 0)
+    khi, grp = (0, 0) if fmt == FMT_FP32 else (KHI, GRP)
     return int(load().qrs_state_pool_bytes(fmt, num_slots, num_heads, DK, DV, khi, grp))
 
 
@@ -132,7 +133,7 @@ class StatePool:
             if arr is not None and arr.shape != shape:
                 raise QrsError(f"{name} must have shape {shape}")
         handle = ctypes.c_void_p()
-        khi, grp = (KHI, GRP) if fmt == FMT_I8F16 else (0, 0)
+        khi, grp = (0, 0) if fmt == FMT_FP32 else (KHI, GRP)
         st = lib.qrs_create_state_pool(
             fmt, num_slots, num_heads, DK, DV, khi, grp, ctypes.c_void_p(self.mem.data_ptr()),
             nbytes,
@@ -233,6 +234,17 @@ def split_units(raw: np.ndarray):
     lo = raw[:, LO_OFFSET:SCALE_OFFSET].copy().view(np.int8).reshape(U, DK - KHI, DV)
     sc = raw[:, SCALE_OFFSET:].copy().view(np.float32).reshape(U, DK - KHI, DV // GRP)
     return hi, lo, sc
+
+
+def split_units_u8h(raw: np.ndarray):
+    """Split packed U8H16 unit bytes [U][20224] into (hi uint16 [U][16][128],
+    codes uint8 [U][112][128], meta uint16 [U][112][4][2] = FP16 (s, z))."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    U = raw.shape[0]
+    hi = raw[:, HI_OFFSET:LO_OFFSET].copy().view(np.uint16).reshape(U, KHI, DV)
+    lo = raw[:, LO_OFFSET:SCALE_OFFSET].copy().reshape(U, DK - KHI, DV)
+    meta = raw[:, SCALE_OFFSET:].copy().view(np.uint16).reshape(U, DK - KHI, DV // GRP, 2)
+    return hi, lo, meta
 
 
 # ---------------------------------------------------------------------------

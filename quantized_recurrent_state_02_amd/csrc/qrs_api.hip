@@ -13,9 +13,10 @@
 #include "qrs_internal.h"
 
 namespace qrs {
-hipError_t launch_decode_i8f16(int kind, const PoolView &pool, const int32_t *slots, int n,
-                               const float *q, const float *k, const float *v, const float *gate,
-                               const float *beta, float *o, hipStream_t stream);
+hipError_t launch_decode_packed(int kind, int codec, const PoolView &pool, const int32_t *slots,
+                                int n, const float *q, const float *k, const float *v,
+                                const float *gate, const float *beta, float *o,
+                                hipStream_t stream);
 hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n,
                              const float *q, const float *k, const float *v, const float *gate,
                              const float *beta, float *o, hipStream_t stream);
@@ -61,7 +62,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool shape_ok(int fmt, int d_k, int d_v, int k_hi, int group) {
     if (d_k != qrs::DK || d_v != qrs::DV) return false;
-    if (fmt == QRS_FMT_I8F16) return k_hi == qrs::KHI && group == qrs::GRP;
+    if (fmt == QRS_FMT_I8F16 || fmt == QRS_FMT_U8H16) return k_hi == qrs::KHI && group == qrs::GRP;
     if (fmt == QRS_FMT_FP32) return k_hi == 0 && group == 0;
     return false;
 }
@@ -70,7 +71,7 @@ bool shape_ok(int fmt, int d_k, int d_v, int k_hi, int group) {
 bool layout(int fmt, int num_slots, int num_heads, size_t *unit_bytes, size_t *perm_off,
             size_t *smooth_off, size_t *total) {
     if (num_slots <= 0 || num_heads <= 0) return false;
-    const size_t ub = fmt == QRS_FMT_I8F16 ? (size_t)qrs::UNIT_BYTES : (size_t)qrs::F32_UNIT_BYTES;
+    const size_t ub = fmt == QRS_FMT_FP32 ? (size_t)qrs::F32_UNIT_BYTES : (size_t)qrs::UNIT_BYTES;
     const size_t units = (size_t)num_slots * (size_t)num_heads;
     if (units > ((size_t)1 << 40) / ub) return false;
     const size_t meta = round_up((size_t)num_heads * qrs::DK * sizeof(int32_t));
@@ -118,9 +119,10 @@ int decode_common(int kind, qrs_pool pool, const int32_t *slots, int n, const fl
     DeviceGuard g(pool->device);
     if (!g.ok) return QRS_EDEVICE;
     const qrs::PoolView pv = view(pool);
-    hipError_t e = pool->fmt == QRS_FMT_I8F16
-                       ? qrs::launch_decode_i8f16(kind, pv, slots, n, q, k, v, gate, beta, o, stream)
-                       : qrs::launch_decode_f32(kind, pv, slots, n, q, k, v, gate, beta, o, stream);
+    hipError_t e = pool->fmt == QRS_FMT_FP32
+                       ? qrs::launch_decode_f32(kind, pv, slots, n, q, k, v, gate, beta, o, stream)
+                       : qrs::launch_decode_packed(kind, pool->fmt == QRS_FMT_U8H16 ? 1 : 0, pv,
+                                                   slots, n, q, k, v, gate, beta, o, stream);
     return e == hipSuccess ? QRS_OK : QRS_EDEVICE;
 }
 
@@ -141,7 +143,7 @@ int qrs_create_state_pool(int fmt, int num_slots, int num_heads, int d_k, int d_
                           const float *smooth_host, hipStream_t stream, qrs_pool *out) {
     if (!out) return QRS_EINVAL;
     *out = nullptr;
-    if (fmt != QRS_FMT_FP32 && fmt != QRS_FMT_I8F16) return QRS_EINVAL;
+    if (fmt != QRS_FMT_FP32 && fmt != QRS_FMT_I8F16 && fmt != QRS_FMT_U8H16) return QRS_EINVAL;
     if (!shape_ok(fmt, d_k, d_v, k_hi, group)) return QRS_EUNSUPPORTED;
     size_t ub, po, so, total;
     if (!layout(fmt, num_slots, num_heads, &ub, &po, &so, &total)) return QRS_EINVAL;
@@ -255,6 +257,7 @@ int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int c
     if (!pool || n < 0 || T < 0 || chunk < 1 || chunk > 64 || (in_dtype != 0 && in_dtype != 1) ||
         (init_from_pool != 0 && init_from_pool != 1))
         return QRS_EINVAL;
+    if (pool->fmt == QRS_FMT_U8H16) return QRS_EUNSUPPORTED;
     if (n == 0 || T == 0) return QRS_OK;
     if (!slots || !q || !k || !v || !alpha || !beta || !o) return QRS_EINVAL;
     if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu || T > (1 << 24)) return QRS_EINVAL;

@@ -7,7 +7,10 @@
 // group s = RN(max|x| / 127), code = RN_int(RN(x / s)).  Model-space input is
 // first mapped to stored coordinates, T[i][j] = S[perm[i]][j] / c[j]
 // (v2 notes, section 2.7).  Same thread mapping as the decode kernels.
-#include "qrs_internal.h"
+// CODEC 1 is the first revision's low tier instead (block-32 Hadamard,
+// asymmetric UINT8 codes, FP16 scale and zero point: HTML section 3.2
+// Eq.(3), Appendix A.1), see qrs_hadamard.h.
+#include "qrs_hadamard.h"
 
 namespace qrs {
 
@@ -41,10 +44,11 @@ __device__ __forceinline__ void load_input_block(const float *Su, const int32_t 
     }
 }
 
-__global__ __launch_bounds__(THREADS) void store_i8f16_kernel(PoolView pool,
-                                                              const int32_t *__restrict__ slots,
-                                                              const float *__restrict__ S,
-                                                              int space) {
+template <int CODEC>
+__global__ __launch_bounds__(THREADS) void store_packed_kernel(PoolView pool,
+                                                               const int32_t *__restrict__ slots,
+                                                               const float *__restrict__ S,
+                                                               int space) {
     const int tid = threadIdx.x;
     const int uu = blockIdx.x;
     const int H = pool.num_heads;
@@ -69,27 +73,49 @@ __global__ __launch_bounds__(THREADS) void store_i8f16_kernel(PoolView pool,
     }
 #pragma unroll
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
-        float amax = 0.f;
-#pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(x[r][c]));
-        amax = pair_max(amax);
-        const float s = group_scale(amax);
-        const double rinv = pack_reciprocal(s);
-        V4 cw;
-        cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
-        cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
-        cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
-        cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
         const int lrow = rg + 16 * (r - 1);
+        V4 cw;
+        uint32_t meta;
+        if (CODEC == 0) {
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(x[r][c]));
+            amax = pair_max(amax);
+            const float s = group_scale(amax);
+            const double rinv = pack_reciprocal(s);
+            cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
+            cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
+            cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
+            cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
+            meta = __builtin_bit_cast(uint32_t, s);
+        } else {
+            hadamard32_pair(x[r], (cb & 1) != 0);
+            float lo = x[r][0], hi = x[r][0];
+#pragma unroll
+            for (int c = 1; c < COLS_PER_THREAD; ++c) {
+                lo = fminf(lo, x[r][c]);
+                hi = fmaxf(hi, x[r][c]);
+            }
+            const U8Params pr = u8_params(lo, hi);
+            float q[COLS_PER_THREAD];
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c) q[c] = u8_code(x[r][c], pr);
+            cw.x = pack4_u8(q[0], q[1], q[2], q[3]);
+            cw.y = pack4_u8(q[4], q[5], q[6], q[7]);
+            cw.z = pack4_u8(q[8], q[9], q[10], q[11]);
+            cw.w = pack4_u8(q[12], q[13], q[14], q[15]);
+            meta = pr.meta;
+        }
         *reinterpret_cast<V4 *>(unit + LO_OFF + lrow * DV + cb * 16) = cw;
         if ((cb & 1) == 0)
-            *reinterpret_cast<float *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4) = s;
+            *reinterpret_cast<uint32_t *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4) = meta;
     }
 }
 
-__global__ __launch_bounds__(THREADS) void dequant_i8f16_kernel(PoolView pool,
-                                                                const int32_t *__restrict__ slots,
-                                                                float *__restrict__ S, int space) {
+template <int CODEC>
+__global__ __launch_bounds__(THREADS) void dequant_packed_kernel(PoolView pool,
+                                                                 const int32_t *__restrict__ slots,
+                                                                 float *__restrict__ S, int space) {
     const int tid = threadIdx.x;
     const int uu = blockIdx.x;
     const int H = pool.num_heads;
@@ -120,11 +146,19 @@ __global__ __launch_bounds__(THREADS) void dequant_i8f16_kernel(PoolView pool,
         } else {
             const int lrow = row - KHI;
             const V4 lw = *reinterpret_cast<const V4 *>(unit + LO_OFF + lrow * DV + cb * 16);
-            const float s =
-                *reinterpret_cast<const float *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4);
+            const uint32_t meta =
+                *reinterpret_cast<const uint32_t *>(unit + SC_OFF + (lrow * NGRP + (cb >> 1)) * 4);
             const uint32_t w4[4] = {lw.x, lw.y, lw.z, lw.w};
+            if (CODEC == 0) {
+                const float s = __builtin_bit_cast(float, meta);
 #pragma unroll
-            for (int c = 0; c < 16; ++c) x[c] = s * sext_byte_to_f32(w4[c >> 2], c & 3);
+                for (int c = 0; c < 16; ++c) x[c] = s * sext_byte_to_f32(w4[c >> 2], c & 3);
+            } else {
+                const float sh = f16_bits_to_f32(meta & 0xffffu), zh = f16_bits_to_f32(meta >> 16);
+#pragma unroll
+                for (int c = 0; c < 16; ++c) x[c] = u8_dequant(w4[c >> 2], c & 3, sh, zh);
+                hadamard32_pair(x, (cb & 1) != 0);
+            }
         }
         int dst = row;
         if (space == 0 && valid) {
@@ -211,7 +245,9 @@ hipError_t launch_store(int fmt, const PoolView &pool, const int32_t *slots, int
                         int space, hipStream_t stream) {
     dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
     if (fmt == 1)
-        hipLaunchKernelGGL(store_i8f16_kernel, grid, block, 0, stream, pool, slots, S, space);
+        hipLaunchKernelGGL(store_packed_kernel<0>, grid, block, 0, stream, pool, slots, S, space);
+    else if (fmt == 2)
+        hipLaunchKernelGGL(store_packed_kernel<1>, grid, block, 0, stream, pool, slots, S, space);
     else
         hipLaunchKernelGGL(store_f32_kernel, grid, block, 0, stream, pool, slots, S, space);
     return hipGetLastError();
@@ -221,7 +257,9 @@ hipError_t launch_dequant(int fmt, const PoolView &pool, const int32_t *slots, i
                           int space, hipStream_t stream) {
     dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
     if (fmt == 1)
-        hipLaunchKernelGGL(dequant_i8f16_kernel, grid, block, 0, stream, pool, slots, S, space);
+        hipLaunchKernelGGL(dequant_packed_kernel<0>, grid, block, 0, stream, pool, slots, S, space);
+    else if (fmt == 2)
+        hipLaunchKernelGGL(dequant_packed_kernel<1>, grid, block, 0, stream, pool, slots, S, space);
     else
         hipLaunchKernelGGL(dequant_f32_kernel, grid, block, 0, stream, pool, slots, S, space);
     return hipGetLastError();

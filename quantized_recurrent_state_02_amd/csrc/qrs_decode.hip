@@ -31,7 +31,7 @@
 // more resident workgroups, one wave per column half over a layout with
 // contiguous column halves, and single 16-byte scale accesses all measured
 // the same or slower.
-#include "qrs_internal.h"
+#include "qrs_hadamard.h"
 
 namespace qrs {
 
@@ -47,8 +47,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 }  // namespace
 
 // KIND 0: GDN (gate = alpha [n][H]); KIND 1: KDA (gate = g [n][H][128]).
-template <int KIND>
-__global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
+// CODEC 0: the INT8 tier (symmetric codes, FP32 scale); CODEC 1: the first
+// revision's tier (block-32 Hadamard, asymmetric UINT8, FP16 scale and zero
+// point; qrs_hadamard.h), read and written at the same offsets.
+template <int KIND, int CODEC>
+__global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     PoolView pool, const int32_t *__restrict__ slots, const float *__restrict__ q,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ gate,
     const float *__restrict__ beta, float *__restrict__ o) {
@@ -136,11 +139,22 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
     }
 #pragma unroll
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
-        const float a = dr[r] * sc_old[r - 1];
         const uint32_t lw[4] = {lo_raw[r - 1].x, lo_raw[r - 1].y, lo_raw[r - 1].z,
                                 lo_raw[r - 1].w};
+        if (CODEC == 0) {
+            const float a = dr[r] * sc_old[r - 1];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[r][c] = a * sext_byte_to_f32(lw[c >> 2], c & 3);
+            for (int c = 0; c < 16; ++c) x[r][c] = a * sext_byte_to_f32(lw[c >> 2], c & 3);
+        } else {
+            // reconstruct in the transformed domain, transform back, then decay
+            const uint32_t m = __builtin_bit_cast(uint32_t, sc_old[r - 1]);
+            const float sh = f16_bits_to_f32(m & 0xffffu), zh = f16_bits_to_f32(m >> 16);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) x[r][c] = u8_dequant(lw[c >> 2], c & 3, sh, zh);
+            hadamard32_pair(x[r], (cb & 1) != 0);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) x[r][c] = dr[r] * x[r][c];
+        }
     }
 
     // ---- partial column reductions over this thread's 8 rows, written to
@@ -207,36 +221,67 @@ __global__ __launch_bounds__(THREADS) void decode_i8f16_kernel(
     // ---- INT8 rows ----
 #pragma unroll
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
-        float amax = 0.f;
-#pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) {
-            x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
-            amax = fmaxf(amax, fabsf(x[r][c]));
-        }
-        amax = pair_max(amax);
-        const float s = group_scale(amax);
-        const double rinv = pack_reciprocal(s);
         U4 cw;
-        cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
-        cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
-        cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
-        cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
+        float meta;
+        if (CODEC == 0) {
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c) {
+                x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
+                amax = fmaxf(amax, fabsf(x[r][c]));
+            }
+            amax = pair_max(amax);
+            const float s = group_scale(amax);
+            const double rinv = pack_reciprocal(s);
+            cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
+            cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
+            cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
+            cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
+            meta = s;
+        } else {
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c)
+                x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
+            hadamard32_pair(x[r], (cb & 1) != 0);
+            float lo = x[r][0], hi = x[r][0];
+#pragma unroll
+            for (int c = 1; c < COLS_PER_THREAD; ++c) {
+                lo = fminf(lo, x[r][c]);
+                hi = fmaxf(hi, x[r][c]);
+            }
+            const U8Params pr = u8_params(lo, hi);
+            float q[COLS_PER_THREAD];
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c) q[c] = u8_code(x[r][c], pr);
+            cw.x = pack4_u8(q[0], q[1], q[2], q[3]);
+            cw.y = pack4_u8(q[4], q[5], q[6], q[7]);
+            cw.z = pack4_u8(q[8], q[9], q[10], q[11]);
+            cw.w = pack4_u8(q[12], q[13], q[14], q[15]);
+            meta = __builtin_bit_cast(float, pr.meta);
+        }
         buf_store16(st, cw, off_lo, LO_OFF + 2048 * (r - 1));
-        if ((cb & 1) == 0) buf_storef(st, s, off_sc + 256 * (r - 1), SC_OFF);
+        if ((cb & 1) == 0) buf_storef(st, meta, off_sc + 256 * (r - 1), SC_OFF);
     }
 }
 
 // Launcher (host): one workgroup per (slot, head) unit.
-hipError_t launch_decode_i8f16(int kind, const PoolView &pool, const int32_t *slots, int n,
-                               const float *q, const float *k, const float *v, const float *gate,
-                               const float *beta, float *o, hipStream_t stream) {
+hipError_t launch_decode_packed(int kind, int codec, const PoolView &pool, const int32_t *slots,
+                                int n, const float *q, const float *k, const float *v,
+                                const float *gate, const float *beta, float *o,
+                                hipStream_t stream) {
     dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
-    if (kind == 0)
-        hipLaunchKernelGGL(decode_i8f16_kernel<0>, grid, block, 0, stream, pool, slots, q, k, v,
-                           gate, beta, o);
+    if (codec == 0 && kind == 0)
+        hipLaunchKernelGGL((decode_packed_kernel<0, 0>), grid, block, 0, stream, pool, slots, q,
+                           k, v, gate, beta, o);
+    else if (codec == 0)
+        hipLaunchKernelGGL((decode_packed_kernel<1, 0>), grid, block, 0, stream, pool, slots, q,
+                           k, v, gate, beta, o);
+    else if (kind == 0)
+        hipLaunchKernelGGL((decode_packed_kernel<0, 1>), grid, block, 0, stream, pool, slots, q,
+                           k, v, gate, beta, o);
     else
-        hipLaunchKernelGGL(decode_i8f16_kernel<1>, grid, block, 0, stream, pool, slots, q, k, v,
-                           gate, beta, o);
+        hipLaunchKernelGGL((decode_packed_kernel<1, 1>), grid, block, 0, stream, pool, slots, q,
+                           k, v, gate, beta, o);
     return hipGetLastError();
 }
 

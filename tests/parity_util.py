@@ -45,12 +45,16 @@ def split_gpu(pool: binding.StatePool, slots) -> tuple:
     raw = pool.units().view(pool.num_slots, H, pool.unit_bytes)[
         torch.as_tensor(np.asarray(slots), dtype=torch.long, device=pool.mem.device)]
     raw = raw.reshape(-1, pool.unit_bytes).cpu().numpy()
+    if pool.fmt == binding.FMT_U8H16:
+        return binding.split_units_u8h(raw)
     return binding.split_units(raw)
 
 
-def oracle_units(opool: oracle.OraclePool, slots):
+def oracle_units(opool, slots):
     H = opool.num_heads
     idx = (np.asarray(slots)[:, None] * H + np.arange(H)[None, :]).ravel()
+    if isinstance(opool, oracle.OracleU8Pool):
+        return opool.hi[idx], opool.lo[idx], opool.meta[idx]
     return opool.hi[idx], opool.lo[idx], opool.sc[idx]
 
 
@@ -69,7 +73,7 @@ def assert_units_equal(g, o, what=""):
     oh, ol, os_ = o
     assert np.array_equal(gh, oh), f"{what}: FP16 rows differ at {np.argwhere(gh != oh)[:4]}"
     assert np.array_equal(gl, ol), f"{what}: codes differ at {np.argwhere(gl != ol)[:4]}"
-    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), f"{what}: scales differ"
+    assert np.array_equal(gs.view(np.uint8), os_.view(np.uint8)), f"{what}: scales differ"
 
 
 class StepBound:
