@@ -52,6 +52,7 @@ PEAK_HBM_GBS = 8000.0
 BYTES_GDN = 20224 * 2 + 3 * 512 + 8
 BYTES_KDA = 20224 * 2 + 3 * 512 + 512 + 4
 BYTES_F32_GDN = 65536 * 2 + 3 * 512 + 8
+BYTES_GDN_BF16IO = 20224 * 2 + 3 * 256 + 8
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gdn_b256_h32_counters.json")
 KERNEL_SOURCES = ["quantized_recurrent_state_02_amd/csrc/qrs_decode.hip",
                   "quantized_recurrent_state_02_amd/csrc/qrs_internal.h"]
@@ -112,7 +113,7 @@ def time_loop(torch, launch, steps, warmup, use_graph):
 
 
 def run_decode(torch, binding, inputs, kind, fmt, dev_in, perm, c, n, H, steps, warmup, pools,
-               use_graph):
+               use_graph, io_bf16=False):
     total_slots = n * pools
     pool = binding.StatePool(fmt, total_slots, H, perm, c)
     cfg = 1 if kind == "gdn" else 2
@@ -123,16 +124,25 @@ def run_decode(torch, binding, inputs, kind, fmt, dev_in, perm, c, n, H, steps, 
         s = torch.arange(p * n, (p + 1) * n, dtype=torch.int32, device="cuda")
         pool.store(s, S0d)
         slot_sets.append(s)
-    out = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
     gate_key = "alpha" if kind == "gdn" else "g"
-    step_fn = pool.gdn_step if kind == "gdn" else pool.kda_step
+    if io_bf16:
+        # q, k, v and the readout in bf16 through qrs_decode_step_ex
+        ops = {x: dev_in[x].to(torch.bfloat16) for x in ("q", "k", "v")}
+        out = torch.empty((n, H, 128), dtype=torch.bfloat16, device="cuda")
 
-    def launch(t):
-        step_fn(slot_sets[t % pools], dev_in["q"][t], dev_in["k"][t], dev_in["v"][t],
-                dev_in[gate_key][t], dev_in["beta"][t], out)
+        def launch(t):
+            pool.step_ex(kind, slot_sets[t % pools], ops["q"][t], ops["k"][t], ops["v"][t],
+                         dev_in[gate_key][t], dev_in["beta"][t], out=out)
+    else:
+        out = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
+        step_fn = pool.gdn_step if kind == "gdn" else pool.kda_step
+
+        def launch(t):
+            step_fn(slot_sets[t % pools], dev_in["q"][t], dev_in["k"][t], dev_in["v"][t],
+                    dev_in[gate_key][t], dev_in["beta"][t], out)
 
     secs = time_loop(torch, launch, steps, warmup, use_graph)
-    ok = bool(torch.isfinite(out).all().item())
+    ok = bool(torch.isfinite(out.float()).all().item())
     pool.close()
     del pool
     torch.cuda.empty_cache()
@@ -351,7 +361,7 @@ def main():
                     help="slot sets rotated per step (4 = cache-cold working set)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gdn", "kda", "f32", "v1", "prefill", "select", "all"],
+    ap.add_argument("--only", choices=["gdn", "kda", "f32", "v1", "bf16", "prefill", "select", "all"],
                     default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
@@ -390,7 +400,7 @@ def main():
     perm1 = inputs.protected_perm(1, H)
     c1 = inputs.smoothing(1, H, True)
     codec_cmp = None
-    if args.only in ("gdn", "f32", "v1", "all"):
+    if args.only in ("gdn", "f32", "v1", "bf16", "all"):
         gdn_in = stage_inputs(torch, inputs, 1, "gdn", n, H, total)
         if args.only in ("gdn", "all"):
             for pools in sorted({args.pools, 1}, reverse=True):
@@ -403,6 +413,11 @@ def main():
                                   c1, n, H, steps, warmup, 1, use_graph)
             res[("f32", 1)] = (secs, ok)
             log(f"[bench] fp32-state gdn: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        if args.only in ("bf16", "all"):
+            secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_I8F16, gdn_in, perm1,
+                                  c1, n, H, steps, warmup, args.pools, use_graph, io_bf16=True)
+            res[("gdnbf16io", args.pools)] = (secs, ok)
+            log(f"[bench] gdn bf16 q/k/v/o pools={args.pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
         if args.only in ("v1", "all"):
             secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_U8H16, gdn_in, perm1,
                                   c1, n, H, steps, warmup, args.pools, use_graph)
@@ -476,7 +491,8 @@ def main():
     out = {}
     head_key = ("gdn", args.pools) if ("gdn", args.pools) in res else next(iter(res))
     kind0 = head_key[0]
-    NB = {"gdn": BYTES_GDN, "gdnv1": BYTES_GDN, "kda": BYTES_KDA, "f32": BYTES_F32_GDN}
+    NB = {"gdn": BYTES_GDN, "gdnv1": BYTES_GDN, "gdnbf16io": BYTES_GDN_BF16IO, "kda": BYTES_KDA,
+          "f32": BYTES_F32_GDN}
     nbytes0 = NB[kind0]
     head = rate(head_key, nbytes0)
     detail = {}
@@ -514,6 +530,7 @@ def main():
         "config": {"workload": {"gdn": "gdn_decode_compressed_state",
                                 "kda": "kda_decode_compressed_state",
                                 "gdnv1": "gdn_decode_u8_hadamard_state",
+                                "gdnbf16io": "gdn_decode_compressed_state_bf16_io",
                                 "f32": "gdn_decode_fp32_state"}[kind0],
                    "batch": n, "heads": H, "d_k": 128, "d_v": 128,
                    "state_format": "16 FP16 + 112 INT8 key rows, FP32 absmax/127 scale per 32",

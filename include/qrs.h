@@ -185,6 +185,23 @@ int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float 
                         float *o, hipStream_t stream);
 
 /*
+ * General decode step: GDN (kind 0) or KDA (kind 1) on heads
+ * [head_begin, head_begin + head_count) of n slots, with q, k, v and o in
+ * FP32 (io_dtype 0) or bf16 (io_dtype 1; inputs widen exactly to FP32, o is
+ * rounded to nearest even from the FP32 readout).  Operands keep their full
+ * [n][H][128] layout (gate: alpha [n][H] or g [n][H][128], FP32; beta [n][H],
+ * FP32) and only the selected heads are read and written, so one slot can
+ * hold GDN heads and KDA heads updated by two calls (the mixed-pool reading
+ * of a GDN/KDA model).  The arithmetic is that of qrs_gdn_decode_step /
+ * qrs_kda_decode_step, which are this call with io_dtype 0 and all heads.
+ * QRS_EINVAL: kind or io_dtype not 0/1, an empty or out-of-range head range.
+ * QRS_EUNSUPPORTED: bf16 I/O on an FP32 pool.
+ */
+int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slots, int n,
+                       int head_begin, int head_count, const void *q, const void *k, const void *v,
+                       const float *gate, const float *beta, void *o, hipStream_t stream);
+
+/*
  * Chunked prefill with GDN gating, writing the compressed state (DAMP arXiv
  * HTML, Appendix A.5 "Prefill path"; v2 reading notes, section 2.2): for each
  * of n sequences (slots[b]) x H heads, runs T tokens through the recurrence

@@ -32,7 +32,7 @@ HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
 EXPORTED = (
     "qrs_state_pool_bytes", "qrs_create_state_pool", "qrs_destroy_state_pool", "qrs_pool_info",
     "qrs_store_state", "qrs_dequant_state", "qrs_gdn_decode_step", "qrs_kda_decode_step",
-    "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
+    "qrs_decode_step_ex", "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
     "qrs_persistence_geometric", "qrs_channel_scores", "qrs_select_protected_channels",
     "qrs_status_string",
 )
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [p, p, i, p, p, p, p, p, p, p]
         fn.restype = i
+    lib.qrs_decode_step_ex.argtypes = [p, i, i, p, i, i, i, p, p, p, p, p, p, p]
+    lib.qrs_decode_step_ex.restype = i
     lib.qrs_chunked_prefill.argtypes = [p, p, i, i, i, i, p, p, p, p, p, p, i, p]
     lib.qrs_chunked_prefill.restype = i
     lib.qrs_channel_error.argtypes = [i, i, p, p, p, p]
@@ -217,6 +219,26 @@ class StatePool:
             _dev(beta, torch.float32, (n, T, H), "beta"),
             _dev(out, torch.float32, (n, T, H, DV), "o"), int(bool(init_from_pool)), _stream())
         _check(st, "qrs_chunked_prefill")
+        return out
+
+    def step_ex(self, kind, slots, q, k, v, gate, beta, heads=None, out=None):
+        """qrs_decode_step_ex: kind "gdn" or "kda"; q, k, v (and out) float32 or
+        bfloat16 [n][H][128]; heads = (begin, count) or None for all."""
+        n, H = slots.numel(), self.num_heads
+        h0, hc = (0, H) if heads is None else (int(heads[0]), int(heads[1]))
+        dt = q.dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise QrsError("q, k, v must be float32 or bfloat16")
+        if out is None:
+            out = torch.full((n, H, DV), float("nan"), dtype=dt, device=self.mem.device)
+        kid = {"gdn": 0, "kda": 1}[kind]
+        gshape = (n, H) if kid == 0 else (n, H, DK)
+        st = load().qrs_decode_step_ex(
+            self.handle, kid, 0 if dt == torch.float32 else 1, _dev(slots, torch.int32, (n,), "slots"),
+            n, h0, hc, _dev(q, dt, (n, H, DK), "q"), _dev(k, dt, (n, H, DK), "k"),
+            _dev(v, dt, (n, H, DV), "v"), _dev(gate, torch.float32, gshape, "gate"),
+            _dev(beta, torch.float32, (n, H), "beta"), _dev(out, dt, (n, H, DV), "o"), _stream())
+        _check(st, "qrs_decode_step_ex")
         return out
 
     def kda_step(self, slots, q, k, v, g, beta, out=None):

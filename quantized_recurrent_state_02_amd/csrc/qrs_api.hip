@@ -13,13 +13,13 @@
 #include "qrs_internal.h"
 
 namespace qrs {
-hipError_t launch_decode_packed(int kind, int codec, const PoolView &pool, const int32_t *slots,
-                                int n, const float *q, const float *k, const float *v,
-                                const float *gate, const float *beta, float *o,
-                                hipStream_t stream);
-hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n,
-                             const float *q, const float *k, const float *v, const float *gate,
-                             const float *beta, float *o, hipStream_t stream);
+hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &pool,
+                                const int32_t *slots, int n, int h0, int hc, const void *q,
+                                const void *k, const void *v, const float *gate, const float *beta,
+                                void *o, hipStream_t stream);
+hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n, int h0,
+                             int hc, const float *q, const float *k, const float *v,
+                             const float *gate, const float *beta, float *o, hipStream_t stream);
 hipError_t launch_store(int fmt, const PoolView &pool, const int32_t *slots, int n, const float *S,
                         int space, hipStream_t stream);
 hipError_t launch_dequant(int fmt, const PoolView &pool, const int32_t *slots, int n, float *S,
@@ -109,20 +109,25 @@ struct DeviceGuard {
     }
 };
 
-int decode_common(int kind, qrs_pool pool, const int32_t *slots, int n, const float *q,
-                  const float *k, const float *v, const float *gate, const float *beta, float *o,
-                  hipStream_t stream) {
-    if (!pool || n < 0) return QRS_EINVAL;
+int decode_common(int kind, int io, qrs_pool pool, const int32_t *slots, int n, int h0, int hc,
+                  const void *q, const void *k, const void *v, const float *gate,
+                  const float *beta, void *o, hipStream_t stream) {
+    if (!pool || n < 0 || (kind != 0 && kind != 1) || (io != 0 && io != 1)) return QRS_EINVAL;
+    if (h0 < 0 || hc < 1 || h0 > pool->num_heads - hc) return QRS_EINVAL;
+    if (pool->fmt == QRS_FMT_FP32 && io != 0) return QRS_EUNSUPPORTED;
     if (n == 0) return QRS_OK;
     if (!slots || !q || !k || !v || !gate || !beta || !o) return QRS_EINVAL;
     if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu) return QRS_EINVAL;
     DeviceGuard g(pool->device);
     if (!g.ok) return QRS_EDEVICE;
     const qrs::PoolView pv = view(pool);
-    hipError_t e = pool->fmt == QRS_FMT_FP32
-                       ? qrs::launch_decode_f32(kind, pv, slots, n, q, k, v, gate, beta, o, stream)
-                       : qrs::launch_decode_packed(kind, pool->fmt == QRS_FMT_U8H16 ? 1 : 0, pv,
-                                                   slots, n, q, k, v, gate, beta, o, stream);
+    hipError_t e =
+        pool->fmt == QRS_FMT_FP32
+            ? qrs::launch_decode_f32(kind, pv, slots, n, h0, hc, static_cast<const float *>(q),
+                                     static_cast<const float *>(k), static_cast<const float *>(v),
+                                     gate, beta, static_cast<float *>(o), stream)
+            : qrs::launch_decode_packed(kind, pool->fmt == QRS_FMT_U8H16 ? 1 : 0, io, pv, slots, n,
+                                        h0, hc, q, k, v, gate, beta, o, stream);
     return e == hipSuccess ? QRS_OK : QRS_EDEVICE;
 }
 
@@ -241,13 +246,22 @@ int qrs_dequant_state(qrs_pool pool, const int32_t *slots, int n, float *S_out, 
 int qrs_gdn_decode_step(qrs_pool pool, const int32_t *slots, int n, const float *q,
                         const float *k, const float *v, const float *alpha, const float *beta,
                         float *o, hipStream_t stream) {
-    return decode_common(0, pool, slots, n, q, k, v, alpha, beta, o, stream);
+    return decode_common(0, 0, pool, slots, n, 0, pool ? pool->num_heads : 1, q, k, v, alpha, beta,
+                         o, stream);
 }
 
 int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float *q,
                         const float *k, const float *v, const float *g, const float *beta,
                         float *o, hipStream_t stream) {
-    return decode_common(1, pool, slots, n, q, k, v, g, beta, o, stream);
+    return decode_common(1, 0, pool, slots, n, 0, pool ? pool->num_heads : 1, q, k, v, g, beta, o,
+                         stream);
+}
+
+int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slots, int n,
+                       int head_begin, int head_count, const void *q, const void *k, const void *v,
+                       const float *gate, const float *beta, void *o, hipStream_t stream) {
+    return decode_common(kind, io_dtype, pool, slots, n, head_begin, head_count, q, k, v, gate,
+                         beta, o, stream);
 }
 
 int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int chunk,

@@ -50,11 +50,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // CODEC 0: the INT8 tier (symmetric codes, FP32 scale); CODEC 1: the first
 // revision's tier (block-32 Hadamard, asymmetric UINT8, FP16 scale and zero
 // point; qrs_hadamard.h), read and written at the same offsets.
-template <int KIND, int CODEC>
+// IO 0: q, k, v, o in FP32; IO 1: in bf16 (gates and beta stay FP32).
+// Workgroup i handles slot b = i / hc, head h0 + i % hc; operands and
+// outputs are indexed [n][H] as for the full head range.
+template <int KIND, int CODEC, int IO>
 __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
-    PoolView pool, const int32_t *__restrict__ slots, const float *__restrict__ q,
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ gate,
-    const float *__restrict__ beta, float *__restrict__ o) {
+    PoolView pool, const int32_t *__restrict__ slots, int h0, int hc, const void *__restrict__ q,
+    const void *__restrict__ k, const void *__restrict__ v, const float *__restrict__ gate,
+    const float *__restrict__ beta, void *__restrict__ o) {
     __shared__ float s_k[DK];
     __shared__ float s_q[DK];
     __shared__ float s_dec[DK];
@@ -64,13 +67,13 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     __shared__ float4 red_z[16][DV / 4];
 
     const int tid = threadIdx.x;
-    const int uu = blockIdx.x;  // b * H + h
     const int H = pool.num_heads;
-    const int b = uu / H;
-    const int h = uu - b * H;
+    const int b = blockIdx.x / hc;
+    const int h = h0 + (blockIdx.x - b * hc);
+    const int uu = b * H + h;
     const int slot = slots[b];
     if (slot < 0 || slot >= pool.num_slots) {
-        o[(size_t)uu * DV + tid] = __builtin_nanf("");
+        st_stream<IO>(o, (size_t)uu * DV + tid, __builtin_nanf(""));
         return;
     }
     const int cb = tid & 7;
@@ -99,15 +102,15 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     // ---- operands: thread t gathers stored row t and owns value column t ----
     const size_t ob = (size_t)uu * DK;
     const int src = pool.perm[h * DK + tid];
-    const float kt = buf_loadf(make_rsrc(k + ob, DK * 4), src * 4, 0);
-    const float qt = buf_loadf(make_rsrc(q + ob, DK * 4), src * 4, 0);
+    const float kt = ld_gather<IO>(k, ob, src);
+    const float qt = ld_gather<IO>(q, ob, src);
     float dec_t;
     if (KIND == 0)
         dec_t = gate[uu];
     else
         dec_t = expf(buf_loadf(make_rsrc(gate + ob, DK * 4), src * 4, 0));
     const float c_t = pool.smooth[h * DV + tid];
-    const float vp_t = __builtin_nontemporal_load(v + ob + tid) / c_t;  // v' = D_c^{-1} v
+    const float vp_t = ld_stream<IO>(v, ob + tid) / c_t;  // v' = D_c^{-1} v
     const float beta_u = beta[uu];
     s_k[tid] = kt;
     s_q[tid] = qt;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
         const float delta = vp_t - w;
         const float bd = beta_u * delta;
         const float qk = s_qk[0] + s_qk[1];
-        __builtin_nontemporal_store(c_t * __builtin_fmaf(qk, bd, z), o + (size_t)uu * DV + tid);
+        st_stream<IO>(o, (size_t)uu * DV + tid, c_t * __builtin_fmaf(qk, bd, z));
         s_bd[tid] = bd;
     }
     __syncthreads();
@@ -264,25 +267,28 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     }
 }
 
-// Launcher (host): one workgroup per (slot, head) unit.
-hipError_t launch_decode_packed(int kind, int codec, const PoolView &pool, const int32_t *slots,
-                                int n, const float *q, const float *k, const float *v,
-                                const float *gate, const float *beta, float *o,
-                                hipStream_t stream) {
-    dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
-    if (codec == 0 && kind == 0)
-        hipLaunchKernelGGL((decode_packed_kernel<0, 0>), grid, block, 0, stream, pool, slots, q,
-                           k, v, gate, beta, o);
-    else if (codec == 0)
-        hipLaunchKernelGGL((decode_packed_kernel<1, 0>), grid, block, 0, stream, pool, slots, q,
-                           k, v, gate, beta, o);
-    else if (kind == 0)
-        hipLaunchKernelGGL((decode_packed_kernel<0, 1>), grid, block, 0, stream, pool, slots, q,
-                           k, v, gate, beta, o);
-    else
-        hipLaunchKernelGGL((decode_packed_kernel<1, 1>), grid, block, 0, stream, pool, slots, q,
-                           k, v, gate, beta, o);
-    return hipGetLastError();
+// Launcher (host): one workgroup per (slot, head) unit of heads [h0, h0 + hc).
+#define QRS_DECODE_CASE(K, C, I)                                                                  \
+    if (kind == K && codec == C && io == I) {                                                     \
+        hipLaunchKernelGGL((decode_packed_kernel<K, C, I>), grid, block, 0, stream, pool, slots,  \
+                           h0, hc, q, k, v, gate, beta, o);                                       \
+        return hipGetLastError();                                                                 \
+    }
+hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &pool,
+                                const int32_t *slots, int n, int h0, int hc, const void *q,
+                                const void *k, const void *v, const float *gate, const float *beta,
+                                void *o, hipStream_t stream) {
+    dim3 grid((unsigned)(n * hc)), block(THREADS);
+    QRS_DECODE_CASE(0, 0, 0)
+    QRS_DECODE_CASE(1, 0, 0)
+    QRS_DECODE_CASE(0, 1, 0)
+    QRS_DECODE_CASE(1, 1, 0)
+    QRS_DECODE_CASE(0, 0, 1)
+    QRS_DECODE_CASE(1, 0, 1)
+    QRS_DECODE_CASE(0, 1, 1)
+    QRS_DECODE_CASE(1, 1, 1)
+    return hipErrorInvalidValue;
 }
+#undef QRS_DECODE_CASE
 
 }  // namespace qrs

@@ -18,7 +18,7 @@ __device__ __forceinline__ float wave_sum_f(float x) {
 
 template <int KIND>
 __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
-    PoolView pool, const int32_t *__restrict__ slots, const float *__restrict__ q,
+    PoolView pool, const int32_t *__restrict__ slots, int h0, int hc, const float *__restrict__ q,
     const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ gate,
     const float *__restrict__ beta, float *__restrict__ o) {
     __shared__ float s_k[DK];
@@ -30,10 +30,10 @@ __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
     __shared__ float4 red_z[16][DV / 4];
 
     const int tid = threadIdx.x;
-    const int uu = blockIdx.x;
     const int H = pool.num_heads;
-    const int b = uu / H;
-    const int h = uu - b * H;
+    const int b = blockIdx.x / hc;  // heads [h0, h0 + hc) of each slot
+    const int h = h0 + (blockIdx.x - b * hc);
+    const int uu = b * H + h;
     const int slot = slots[b];
     if (slot < 0 || slot >= pool.num_slots) {
         o[(size_t)uu * DV + tid] = __builtin_nanf("");
@@ -142,16 +142,16 @@ __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
     }
 }
 
-hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n,
-                             const float *q, const float *k, const float *v, const float *gate,
-                             const float *beta, float *o, hipStream_t stream) {
-    dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
+hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n, int h0,
+                             int hc, const float *q, const float *k, const float *v,
+                             const float *gate, const float *beta, float *o, hipStream_t stream) {
+    dim3 grid((unsigned)(n * hc)), block(THREADS);
     if (kind == 0)
-        hipLaunchKernelGGL(decode_f32_kernel<0>, grid, block, 0, stream, pool, slots, q, k, v,
-                           gate, beta, o);
+        hipLaunchKernelGGL(decode_f32_kernel<0>, grid, block, 0, stream, pool, slots, h0, hc, q, k,
+                           v, gate, beta, o);
     else
-        hipLaunchKernelGGL(decode_f32_kernel<1>, grid, block, 0, stream, pool, slots, q, k, v,
-                           gate, beta, o);
+        hipLaunchKernelGGL(decode_f32_kernel<1>, grid, block, 0, stream, pool, slots, h0, hc, q, k,
+                           v, gate, beta, o);
     return hipGetLastError();
 }
 

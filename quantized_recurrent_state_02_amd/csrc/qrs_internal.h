@@ -226,4 +226,33 @@ __device__ __forceinline__ void buf_storef(__amdgpu_buffer_rsrc_t r, float d, in
                                           kStream);
 }
 
+// ---- operand I/O in FP32 or bf16 (IO = 0 / 1) ---------------------------
+// bf16 operands widen exactly to FP32; bf16 outputs are rounded to nearest
+// even from the FP32 result (a NaN stays a quiet NaN).
+template <int IO>
+__device__ __forceinline__ float ld_gather(const void *base, size_t ob, int i) {
+    if (IO == 0) return buf_loadf(make_rsrc(static_cast<const float *>(base) + ob, DK * 4), i * 4, 0);
+    const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(
+        make_rsrc(static_cast<const uint16_t *>(base) + ob, DK * 2), i * 2, 0, kStream);
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+template <int IO>
+__device__ __forceinline__ float ld_stream(const void *base, size_t idx) {
+    if (IO == 0) return __builtin_nontemporal_load(static_cast<const float *>(base) + idx);
+    const uint16_t bits = __builtin_nontemporal_load(static_cast<const uint16_t *>(base) + idx);
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+template <int IO>
+__device__ __forceinline__ void st_stream(void *base, size_t idx, float v) {
+    if (IO == 0)
+        __builtin_nontemporal_store(v, static_cast<float *>(base) + idx);
+    else
+        __builtin_nontemporal_store(f32_to_bf16_rne(v), static_cast<uint16_t *>(base) + idx);
+}
+
 }  // namespace qrs

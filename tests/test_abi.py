@@ -156,3 +156,8 @@ def test_select_protected_matches_oracle():
         sc = np.where(np.isnan(score), -np.inf, score)
         _, want = selector.select_protected(sc, k)
         assert np.array_equal(perm, want), k
+
+
+def test_decode_step_ex_rejects_null_pool(lib):
+    p = ctypes.c_void_p(0x10000)
+    assert lib.qrs_decode_step_ex(None, 0, 0, p, 1, 0, 1, p, p, p, p, p, p, None) == -1
