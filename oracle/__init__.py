@@ -294,3 +294,52 @@ class OracleU8Pool:
                              _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, kind,
                              _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(o))
         return o
+
+
+class OracleWindowPool:
+    """Per-window quantization on the packed pool ("LeapQuant: Efficient Linear
+    Attention with Accurate Recurrent State Quantization", section 3.2 and
+    Figure 2; memory figures of section 4.3).
+
+    The stored (quantized) state of a slot is held fixed for a window of
+    ``window`` tokens.  Every token of the window is recorded with its k and
+    v rounded to FP16 (beta and the gate in FP32), and each output is that of
+    the FP32 recurrence started from the dequantized window-start state and
+    run through the window's records up to and including the current token,
+    read out with the current q.  The token that completes the window stores
+    the resulting FP32 state back into the pool (requantized), which starts
+    the next window.  ``pos[b]`` is the index of this token in slot b's
+    window; calls must visit positions 0, 1, ..., window - 1 in order.
+    Window 1 is the per-step method of OraclePool with FP16-rounded k and v.
+    """
+
+    def __init__(self, num_slots, num_heads, perm=None, c=None, window=16):
+        self.pool = OraclePool(num_slots, num_heads, perm, c)
+        self.window = window
+        self.num_heads = num_heads
+        self.records = {}
+
+    def store(self, slots, S, space=0):
+        self.pool.store(slots, S, space)
+        for s in np.asarray(slots).tolist():
+            self.records[s] = []
+
+    def step(self, slots, pos, q, k, v, gate, beta, kind):
+        H = self.num_heads
+        q, k, v, gate, beta = (_f32(a) for a in (q, k, v, gate, beta))
+        out = np.empty((len(slots), H, DV), dtype=np.float32)
+        for b, s in enumerate(np.asarray(slots).tolist()):
+            recs = self.records.setdefault(s, [])
+            assert len(recs) == int(pos[b]), "window positions must advance one token at a time"
+            k16 = f16_bits_to_f32(f32_to_f16_bits(k[b]))
+            v16 = f16_bits_to_f32(f32_to_f16_bits(v[b]))
+            recs.append((k16, v16, gate[b].copy(), beta[b].copy()))
+            dense = OracleDensePool(1, H, self.pool.perm, self.pool.c)
+            dense.T[:] = self.pool.dequant([s], space=1)[0]
+            for kk, vv, gg, bb in recs:
+                o = dense.decode_step([0], q[b:b + 1], kk[None], vv[None], gg[None], bb[None], kind)
+            out[b] = o[0]
+            if len(recs) == self.window:
+                self.pool.store([s], dense.T.reshape(1, H, DK, DV), space=1)
+                self.records[s] = []
+        return out
