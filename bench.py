@@ -242,6 +242,40 @@ def run_codec_compare(torch, binding, inputs, dev_in, perm, c, n, H, steps):
     return res
 
 
+# Per-window quantization (LeapQuant section 3.2): algorithmic bytes per GDN
+# update averaged over a 16-token window -- the state read every token, written
+# once per window, the window's records (528 B: k, v FP16, beta, alpha) read
+# (7.5 on average) and written (15 of 16 tokens), q, k, v and gates.
+WINDOW = 16
+BYTES_GDN_WINDOW = (20224 + 20224 / WINDOW + 528 * (WINDOW - 1) / 2 + 528 * (WINDOW - 1) / WINDOW
+                    + 3 * 512 + 8)
+
+
+def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph, reps=16):
+    """GDN per-window decode at the serving shape, every slot in the same phase,
+    `reps` whole windows timed; returns (seconds per token step, ok)."""
+    pool = binding.StatePool(binding.FMT_I8F16, n, H, perm, c)
+    slots = torch.arange(n, dtype=torch.int32, device="cuda")
+    pool.store(slots, torch.from_numpy(inputs.initial_state(1, n, H)).to("cuda"))
+    buf = pool.window_buffer("gdn", WINDOW)
+    pos = [torch.full((n,), j, dtype=torch.int32, device="cuda") for j in range(WINDOW)]
+    out = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
+    T = dev_in["q"].shape[0]
+
+    def launch(t):
+        tt = t % T
+        pool.window_step("gdn", WINDOW, buf, slots, pos[t % WINDOW], dev_in["q"][tt],
+                         dev_in["k"][tt], dev_in["v"][tt], dev_in["alpha"][tt], dev_in["beta"][tt],
+                         out=out)
+
+    steps = reps * WINDOW
+    secs = time_loop(torch, launch, steps, WINDOW, use_graph)
+    ok = bool(torch.isfinite(out).all().item())
+    pool.close()
+    torch.cuda.empty_cache()
+    return secs / steps, ok
+
+
 # Key-channel selection, calibration-shaped: 32 sequences of 256 steps, 32
 # heads, one sampled state every 8 steps (1,024 samples per head).  The error
 # kernel reads every sampled FP32 state once (64 KiB per sample and head).
@@ -361,7 +395,8 @@ def main():
                     help="slot sets rotated per step (4 = cache-cold working set)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gdn", "kda", "f32", "v1", "bf16", "prefill", "select", "all"],
+    ap.add_argument("--only", choices=["gdn", "kda", "f32", "v1", "bf16", "window", "prefill",
+                                       "select", "all"],
                     default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
@@ -400,7 +435,8 @@ def main():
     perm1 = inputs.protected_perm(1, H)
     c1 = inputs.smoothing(1, H, True)
     codec_cmp = None
-    if args.only in ("gdn", "f32", "v1", "bf16", "all"):
+    window_res = None
+    if args.only in ("gdn", "f32", "v1", "bf16", "window", "all"):
         gdn_in = stage_inputs(torch, inputs, 1, "gdn", n, H, total)
         if args.only in ("gdn", "all"):
             for pools in sorted({args.pools, 1}, reverse=True):
@@ -418,6 +454,17 @@ def main():
                                   c1, n, H, steps, warmup, args.pools, use_graph, io_bf16=True)
             res[("gdnbf16io", args.pools)] = (secs, ok)
             log(f"[bench] gdn bf16 q/k/v/o pools={args.pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        if args.only in ("window", "all"):
+            sec_w, ok_w = run_window(torch, binding, inputs, gdn_in, perm1, c1, n, H, warmup,
+                                     use_graph)
+            window_res = {"workload": f"GDN, {n} slots x {H} heads, windows of {WINDOW} tokens, "
+                                      "all slots in phase, 16 windows timed",
+                          "us_per_step": sec_w * 1e6, "updates_per_s": n * H / sec_w,
+                          "bytes_per_update": BYTES_GDN_WINDOW,
+                          "gbs": n * H * BYTES_GDN_WINDOW / sec_w / 1e9,
+                          "frac_of_peak": n * H * BYTES_GDN_WINDOW / sec_w / 1e9 / PEAK_HBM_GBS,
+                          "finite_outputs": ok_w}
+            log(f"[bench] gdn per-window (16): {sec_w * 1e6:.2f} us/step ok={ok_w}")
         if args.only in ("v1", "all"):
             secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_U8H16, gdn_in, perm1,
                                   c1, n, H, steps, warmup, args.pools, use_graph)
@@ -463,6 +510,16 @@ def main():
                 "gbs": ups * nbytes / 1e9, "frac_of_peak": ups * nbytes / 1e9 / PEAK_HBM_GBS,
                 "finite_outputs": ok}
 
+    if not res and window_res:   # --only window: a diagnostic line for per-window decode
+        print(json.dumps({"metric": "per-window decode: state updates/s (windows of 16 tokens)",
+                          "value": window_res["updates_per_s"], "unit": "state updates/s",
+                          "n_gpus": 1, "higher_is_better": True, "dtype": "f32",
+                          "data": "synthetic", "config": {"workload": window_res["workload"]},
+                          "roofline": {"bound": "hbm", "achieved": window_res["gbs"],
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": window_res["frac_of_peak"], "traffic": None},
+                          "detail": {"window": window_res}}))
+        return
     if not res and select:   # --only select: a diagnostic line for the selection kernels
         print(json.dumps({"metric": "key-channel selection: calibration states scored per second",
                           "value": 1024 / (select["channel_error_ms"] / 1e3),
@@ -507,6 +564,8 @@ def main():
         detail["select"] = select
     if codec_cmp:
         detail["codec_comparison"] = codec_cmp
+    if window_res:
+        detail["window"] = window_res
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -202,6 +202,37 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
                        const float *gate, const float *beta, void *o, hipStream_t stream);
 
 /*
+ * Per-window quantization ("LeapQuant: Efficient Linear Attention with
+ * Accurate Recurrent State Quantization", section 3.2, Figure 2; buffer size
+ * of section 4.3) on a QRS_FMT_I8F16 pool.  The stored state of a slot stays
+ * fixed for `window` tokens (1..32; the pages use 16 and find no gain at 32).  Each token of the
+ * window is recorded in a caller-owned update buffer with k and v rounded to
+ * FP16 (nearest even) and beta and the gate in FP32; the output of token j
+ * is that of the FP32 recurrence of qrs_gdn_decode_step / qrs_kda_decode_step
+ * started from the dequantized window-start state and run through the
+ * window's tokens 0..j (FP16 k and v), read out with this token's q.  The
+ * token at position window - 1 writes the requantized end state into the
+ * pool, which starts the next window; the others write only their record.
+ *   kind: 0 GDN (gate = alpha [n][H]), 1 KDA (gate = g [n][H][128]);
+ *   buffer: device memory of >= qrs_window_buffer_bytes(kind, num_slots,
+ *     num_heads, window) bytes, 16-byte aligned, laid out as
+ *     [num_slots][num_heads][window] records of 528 B (GDN: k FP16[128],
+ *     v FP16[128], beta, alpha) or 1,040 B (KDA: k, v, g FP32[128], beta);
+ *   pos: int32 [n] device, the index of this token in slot b's window.
+ *     Calls must visit positions 0, 1, ..., window - 1 of a slot in order
+ *     (position 0 starts from the pool's stored state); a slot id or
+ *     position out of range leaves everything untouched and gives NaN
+ *     outputs.
+ * q, k, v, o: FP32 [n][H][128] as for the other decode calls.
+ * QRS_EUNSUPPORTED on other pool formats.
+ */
+size_t qrs_window_buffer_bytes(int kind, int num_slots, int num_heads, int window);
+int qrs_window_decode_step(qrs_pool pool, int kind, int window, void *buffer, size_t buffer_bytes,
+                           const int32_t *slots, const int32_t *pos, int n, const float *q,
+                           const float *k, const float *v, const float *gate, const float *beta,
+                           float *o, hipStream_t stream);
+
+/*
  * Chunked prefill with GDN gating, writing the compressed state (DAMP arXiv
  * HTML, Appendix A.5 "Prefill path"; v2 reading notes, section 2.2): for each
  * of n sequences (slots[b]) x H heads, runs T tokens through the recurrence

@@ -32,7 +32,8 @@ HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
 EXPORTED = (
     "qrs_state_pool_bytes", "qrs_create_state_pool", "qrs_destroy_state_pool", "qrs_pool_info",
     "qrs_store_state", "qrs_dequant_state", "qrs_gdn_decode_step", "qrs_kda_decode_step",
-    "qrs_decode_step_ex", "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
+    "qrs_decode_step_ex", "qrs_window_buffer_bytes", "qrs_window_decode_step",
+    "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
     "qrs_persistence_geometric", "qrs_channel_scores", "qrs_select_protected_channels",
     "qrs_status_string",
 )
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH):
         fn.restype = i
     lib.qrs_decode_step_ex.argtypes = [p, i, i, p, i, i, i, p, p, p, p, p, p, p]
     lib.qrs_decode_step_ex.restype = i
+    lib.qrs_window_buffer_bytes.argtypes = [i, i, i, i]
+    lib.qrs_window_buffer_bytes.restype = sz
+    lib.qrs_window_decode_step.argtypes = [p, i, i, p, sz, p, p, i, p, p, p, p, p, p, p]
+    lib.qrs_window_decode_step.restype = i
     lib.qrs_chunked_prefill.argtypes = [p, p, i, i, i, i, p, p, p, p, p, p, i, p]
     lib.qrs_chunked_prefill.restype = i
     lib.qrs_channel_error.argtypes = [i, i, p, p, p, p]
@@ -239,6 +244,34 @@ class StatePool:
             _dev(v, dt, (n, H, DV), "v"), _dev(gate, torch.float32, gshape, "gate"),
             _dev(beta, torch.float32, (n, H), "beta"), _dev(out, dt, (n, H, DV), "o"), _stream())
         _check(st, "qrs_decode_step_ex")
+        return out
+
+    def window_buffer(self, kind: str, window: int) -> torch.Tensor:
+        """A zeroed device update buffer for window_step (uint8)."""
+        nb = int(load().qrs_window_buffer_bytes({"gdn": 0, "kda": 1}[kind], self.num_slots,
+                                                self.num_heads, int(window)))
+        if nb == 0:
+            raise QrsError("invalid window buffer shape")
+        return torch.zeros(nb, dtype=torch.uint8, device=self.mem.device)
+
+    def window_step(self, kind, window, buffer, slots, pos, q, k, v, gate, beta, out=None):
+        """qrs_window_decode_step: one token per slot at window positions pos
+        (int32 [n]); q, k, v float32 [n][H][128]."""
+        n, H = slots.numel(), self.num_heads
+        kid = {"gdn": 0, "kda": 1}[kind]
+        if out is None:
+            out = torch.empty((n, H, DV), dtype=torch.float32, device=self.mem.device)
+        if not (isinstance(buffer, torch.Tensor) and buffer.is_cuda and buffer.dtype == torch.uint8):
+            raise QrsError("buffer must be a device uint8 tensor")
+        gshape = (n, H) if kid == 0 else (n, H, DK)
+        st = load().qrs_window_decode_step(
+            self.handle, kid, int(window), ctypes.c_void_p(buffer.data_ptr()), buffer.numel(),
+            _dev(slots, torch.int32, (n,), "slots"), _dev(pos, torch.int32, (n,), "pos"), n,
+            _dev(q, torch.float32, (n, H, DK), "q"), _dev(k, torch.float32, (n, H, DK), "k"),
+            _dev(v, torch.float32, (n, H, DV), "v"), _dev(gate, torch.float32, gshape, "gate"),
+            _dev(beta, torch.float32, (n, H), "beta"), _dev(out, torch.float32, (n, H, DV), "o"),
+            _stream())
+        _check(st, "qrs_window_decode_step")
         return out
 
     def kda_step(self, slots, q, k, v, g, beta, out=None):

@@ -28,6 +28,10 @@ hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, i
                           int chunk, int in_bf16, const void *q, const void *k, const void *v,
                           const float *alpha, const float *beta, float *o, int init_from_pool,
                           hipStream_t stream);
+hipError_t launch_window(int kind, const PoolView &pool, uint8_t *buf, int window,
+                         const int32_t *slots, const int32_t *pos, int n, const float *q,
+                         const float *k, const float *v, const float *gate, const float *beta,
+                         float *o, hipStream_t stream);
 hipError_t launch_channel_error(int n, int num_heads, const float *S, const float *smooth,
                                 double *e, hipStream_t stream);
 hipError_t launch_persistence_window(int n_seq, int T, int num_heads, const float *a, int n,
@@ -262,6 +266,35 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
                        const float *gate, const float *beta, void *o, hipStream_t stream) {
     return decode_common(kind, io_dtype, pool, slots, n, head_begin, head_count, q, k, v, gate,
                          beta, o, stream);
+}
+
+size_t qrs_window_buffer_bytes(int kind, int num_slots, int num_heads, int window) {
+    if ((kind != 0 && kind != 1) || num_slots <= 0 || num_heads <= 0 || window < 1 || window > 32)
+        return 0;
+    const size_t rec = kind == 0 ? 528 : 1040;
+    const size_t units = (size_t)num_slots * (size_t)num_heads;
+    if (units > ((size_t)1 << 40) / (rec * (size_t)window)) return 0;
+    return units * (size_t)window * rec;
+}
+
+int qrs_window_decode_step(qrs_pool pool, int kind, int window, void *buffer, size_t buffer_bytes,
+                           const int32_t *slots, const int32_t *pos, int n, const float *q,
+                           const float *k, const float *v, const float *gate, const float *beta,
+                           float *o, hipStream_t stream) {
+    if (!pool || n < 0 || (kind != 0 && kind != 1) || window < 1 || window > 32) return QRS_EINVAL;
+    if (pool->fmt != QRS_FMT_I8F16) return QRS_EUNSUPPORTED;
+    const size_t need = qrs_window_buffer_bytes(kind, pool->num_slots, pool->num_heads, window);
+    if (!buffer || need == 0 || buffer_bytes < need) return QRS_EINVAL;
+    if (reinterpret_cast<uintptr_t>(buffer) % 16 != 0) return QRS_EINVAL;
+    if (n == 0) return QRS_OK;
+    if (!slots || !pos || !q || !k || !v || !gate || !beta || !o) return QRS_EINVAL;
+    if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu) return QRS_EINVAL;
+    DeviceGuard g(pool->device);
+    if (!g.ok) return QRS_EDEVICE;
+    return qrs::launch_window(kind, view(pool), static_cast<uint8_t *>(buffer), window, slots, pos,
+                              n, q, k, v, gate, beta, o, stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
 }
 
 int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int chunk,

@@ -1,0 +1,343 @@
+// qrs_window.hip -- per-window quantization on the packed pool ("LeapQuant:
+// Efficient Linear Attention with Accurate Recurrent State Quantization",
+// section 3.2 and Figure 2): the stored state of a slot stays fixed for a
+// window of tokens, each token's update is kept in a small buffer (k and v in
+// FP16, beta and the gate in FP32), outputs come from the fixed state and the
+// buffered updates, and the token that completes the window writes the
+// requantized state.
+//
+// One 128-thread workgroup per (slot, head), the decode kernels' mapping
+// (thread = 8 rows x 16 columns of the FP32 state).  With S_0 the dequantized
+// window-start state (stored coordinates) and tokens 1..j of the window,
+//   S_j^T q = S_0^T x_0 + sum_t v'_t beta_t (k'_t . x_t),
+//   x_j = q',  x_{t-1} = Lambda_t (x_t - beta_t k'_t (k'_t . x_t)),
+// which follows from S_t = (I - beta k k^T) Lambda S_{t-1} + beta k v^T
+// (HTML of DAMP, section 3.1, Eq.(2)); so a step inside the window costs one
+// matrix-vector product over the stored state plus O(j d) vector work, and
+// writes only its 528-byte (GDN) / 1,040-byte (KDA) record.  The step that
+// completes the window replays the window's updates on the state in
+// registers (the recurrence of the decode kernels, token by token), reads
+// out, and requantizes into the pool.
+//
+// Record of token t of slot s, head h, at buffer + ((s H + h) window + t) R:
+//   [0, 256) k FP16 [128], [256, 512) v FP16 [128] (model order);
+//   GDN (R = 528): [512] beta, [516] alpha (FP32);
+//   KDA (R = 1040): [512, 1024) g FP32 [128], [1024] beta.
+#include "qrs_internal.h"
+
+namespace qrs {
+
+constexpr int WIN_MAX = 32;
+
+__host__ __device__ constexpr int window_record_bytes(int kind) { return kind == 0 ? 528 : 1040; }
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Fields of a record staged in LDS (the record layout, byte offsets).
+__device__ __forceinline__ float lds_f16(const uint8_t *base, int byte_off) {
+    return f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(base + byte_off));
+}
+__device__ __forceinline__ float lds_f32(const uint8_t *base, int byte_off) {
+    return *reinterpret_cast<const float *>(base + byte_off);
+}
+
+}  // namespace
+
+template <int KIND>
+__global__ __launch_bounds__(THREADS) void window_kernel(
+    PoolView pool, uint8_t *__restrict__ buf, int window, const int32_t *__restrict__ slots,
+    const int32_t *__restrict__ pos, const float *__restrict__ q, const float *__restrict__ k,
+    const float *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta,
+    float *__restrict__ o) {
+    constexpr int R = window_record_bytes(KIND);
+    __shared__ float s_kc[DK];     // current token's k (FP16-rounded), model order
+    __shared__ float s_q[DK];      // q, model order
+    __shared__ float s_lam[DK];    // KDA: exp(g) of the token being processed, model order
+    __shared__ int s_perm[DK];
+    __shared__ float s_x0[DK];     // back-propagated query, stored order
+    __shared__ float s_coef[WIN_MAX];
+    __shared__ float s_bd[DV];
+    __shared__ float s_qk[2];
+    __shared__ float4 red_w[16][DV / 4];
+    __shared__ float4 red_z[16][DV / 4];
+    extern __shared__ __align__(16) uint8_t s_rec[];  // this window's earlier records, window * R bytes
+
+    const int tid = threadIdx.x;
+    const int uu = blockIdx.x;
+    const int H = pool.num_heads;
+    const int b = uu / H;
+    const int h = uu - b * H;
+    const int slot = slots[b];
+    const int p = pos[b];
+    if (slot < 0 || slot >= pool.num_slots || p < 0 || p >= window) {
+        o[(size_t)uu * DV + tid] = __builtin_nanf("");
+        return;
+    }
+    const bool boundary = p == window - 1;
+    const int cb = tid & 7;
+    const int rg = tid >> 3;
+    const __amdgpu_buffer_rsrc_t st =
+        make_rsrc(pool.base + ((size_t)slot * H + h) * UNIT_BYTES, UNIT_BYTES);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(buf + ((size_t)slot * H + h) * (size_t)window * R, window * R);
+    const int off_hi = HI_OFF + rg * (DV * 2) + cb * 32;
+    const int off_lo = rg * DV + cb * 16;
+    const int off_sc = (rg * NGRP + (cb >> 1)) * 4;
+
+    // ---- the window-start state ----
+    U4 hi_raw[2];
+    U4 lo_raw[ROWS_PER_THREAD - 1];
+    float sc_old[ROWS_PER_THREAD - 1];
+    hi_raw[0] = buf_load16(st, off_hi, 0);
+    hi_raw[1] = buf_load16(st, off_hi + 16, 0);
+#pragma unroll
+    for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+        lo_raw[r - 1] = buf_load16(st, off_lo, LO_OFF + 2048 * (r - 1));
+        sc_old[r - 1] = buf_loadf(st, off_sc + 256 * (r - 1), SC_OFF);
+    }
+
+    // ---- this window's earlier records (p * R bytes) into LDS, 16 B per lane ----
+    for (int e = tid; e < p * (R / 16); e += THREADS)
+        *reinterpret_cast<U4 *>(s_rec + 16 * e) = buf_load16(rb, 16 * e, 0);
+
+    // ---- the current token: FP16 k and v, recorded unless it ends the window ----
+    const size_t ob = (size_t)uu * DK;
+    const uint32_t k16 = f32_to_f16_bits(k[ob + tid]);
+    const uint32_t v16 = f32_to_f16_bits(v[ob + tid]);
+    const float c_t = pool.smooth[h * DV + tid];
+    const float beta_c = beta[uu];
+    const float alpha_c = KIND == 0 ? gate[uu] : 0.f;
+    const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
+    if (!boundary) {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k16, rb, p * R + 2 * tid, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v16, rb, p * R + 256 + 2 * tid, 0, 0);
+        if (KIND == 1) buf_storef(rb, g_c, p * R + 512 + 4 * tid, 0);
+        if (tid == 0) {
+            buf_storef(rb, beta_c, p * R + (KIND == 0 ? 512 : 1024), 0);
+            if (KIND == 0) buf_storef(rb, alpha_c, p * R + 516, 0);
+        }
+    }
+    s_kc[tid] = f16_bits_to_f32(k16);
+    s_q[tid] = q[ob + tid];
+    s_perm[tid] = pool.perm[h * DK + tid];
+    if (KIND == 1) s_lam[tid] = expf(g_c);
+    const float vc = f16_bits_to_f32(v16) / c_t;  // v' of the current token, column tid
+    __syncthreads();
+
+    // ---- dequantize (no decay: decays come with each token) ----
+    float x[ROWS_PER_THREAD][COLS_PER_THREAD];
+    {
+        const uint32_t hw[8] = {hi_raw[0].x, hi_raw[0].y, hi_raw[0].z, hi_raw[0].w,
+                                hi_raw[1].x, hi_raw[1].y, hi_raw[1].z, hi_raw[1].w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            x[0][2 * c] = f16_bits_to_f32(hw[c] & 0xffffu);
+            x[0][2 * c + 1] = f16_bits_to_f32(hw[c] >> 16);
+        }
+    }
+#pragma unroll
+    for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+        const uint32_t lw[4] = {lo_raw[r - 1].x, lo_raw[r - 1].y, lo_raw[r - 1].z,
+                                lo_raw[r - 1].w};
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[r][c] = sc_old[r - 1] * sext_byte_to_f32(lw[c >> 2], c & 3);
+    }
+
+    if (!boundary) {
+        // ---- wave 0: back-propagate the query through tokens p, p-1, ..., 0 ----
+        if (tid < 64) {
+            const int i0 = tid, i1 = tid + 64;  // stored rows of this lane
+            const int m0 = s_perm[i0], m1 = s_perm[i1];
+            float x0 = s_q[m0], x1 = s_q[m1];
+            for (int t = p; t >= 0; --t) {
+                float ka, kb, la, lb, bt;
+                if (t == p) {
+                    ka = s_kc[m0];
+                    kb = s_kc[m1];
+                    bt = beta_c;
+                    la = KIND == 0 ? alpha_c : s_lam[m0];
+                    lb = KIND == 0 ? alpha_c : s_lam[m1];
+                } else {
+                    const uint8_t *rec = s_rec + t * R;
+                    ka = lds_f16(rec, 2 * m0);
+                    kb = lds_f16(rec, 2 * m1);
+                    bt = lds_f32(rec, KIND == 0 ? 512 : 1024);
+                    if (KIND == 0) {
+                        la = lb = lds_f32(rec, 516);
+                    } else {
+                        la = expf(lds_f32(rec, 512 + 4 * m0));
+                        lb = expf(lds_f32(rec, 512 + 4 * m1));
+                    }
+                }
+                const float coef = bt * wave_sum(__builtin_fmaf(ka, x0, kb * x1));
+                if (tid == 0) s_coef[t] = coef;
+                x0 = la * (x0 - coef * ka);
+                x1 = lb * (x1 - coef * kb);
+            }
+            s_x0[i0] = x0;
+            s_x0[i1] = x1;
+        }
+        __syncthreads();
+        // ---- z = S_0^T x_0 ----
+        float xr[ROWS_PER_THREAD];
+#pragma unroll
+        for (int r = 0; r < ROWS_PER_THREAD; ++r) xr[r] = s_x0[rg + 16 * r];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            float pz[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 4 * c4 + j;
+                float az = xr[0] * x[0][c];
+#pragma unroll
+                for (int r = 1; r < ROWS_PER_THREAD; ++r) az = __builtin_fmaf(xr[r], x[r][c], az);
+                pz[j] = az;
+            }
+            red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
+        }
+        __syncthreads();
+        const float *rz = reinterpret_cast<const float *>(red_z);
+        float z = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) z += rz[g * DV + tid];
+        // the buffered writes: sum_t v'_t coef_t (column tid)
+        float acc = s_coef[p] * vc;
+        for (int t = 0; t < p; ++t)
+            acc = __builtin_fmaf(s_coef[t], lds_f16(s_rec + t * R, 256 + 2 * tid) / c_t, acc);
+        __builtin_nontemporal_store(c_t * (z + acc), o + (size_t)uu * DV + tid);
+        return;
+    }
+
+    // ---- the window's last token: replay tokens 0..p on the state ----
+    {
+        const float pqk = wave_sum(s_q[tid] * f16_bits_to_f32(k16));
+        if ((tid & 63) == 0) s_qk[tid >> 6] = pqk;
+    }
+    for (int t = 0; t <= p; ++t) {
+        float kr[ROWS_PER_THREAD], dr[ROWS_PER_THREAD], bt, vp;
+        if (t < p) {
+            const uint8_t *rec = s_rec + t * R;
+            vp = lds_f16(rec, 256 + 2 * tid) / c_t;
+            bt = lds_f32(rec, KIND == 0 ? 512 : 1024);
+            const float at = KIND == 0 ? lds_f32(rec, 516) : 0.f;
+#pragma unroll
+            for (int r = 0; r < ROWS_PER_THREAD; ++r) {
+                const int m = s_perm[rg + 16 * r];
+                kr[r] = lds_f16(rec, 2 * m);
+                dr[r] = KIND == 0 ? at : expf(lds_f32(rec, 512 + 4 * m));
+            }
+        } else {
+            vp = vc;
+            bt = beta_c;
+#pragma unroll
+            for (int r = 0; r < ROWS_PER_THREAD; ++r) {
+                const int m = s_perm[rg + 16 * r];
+                kr[r] = s_kc[m];
+                dr[r] = KIND == 0 ? alpha_c : s_lam[m];
+            }
+        }
+        float qr[ROWS_PER_THREAD];
+        if (t == p) {
+#pragma unroll
+            for (int r = 0; r < ROWS_PER_THREAD; ++r) qr[r] = s_q[s_perm[rg + 16 * r]];
+        }
+#pragma unroll
+        for (int r = 0; r < ROWS_PER_THREAD; ++r)
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c) x[r][c] = dr[r] * x[r][c];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            float pw[4], pz[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 4 * c4 + j;
+                float aw = kr[0] * x[0][c];
+                float az = t == p ? qr[0] * x[0][c] : 0.f;
+#pragma unroll
+                for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+                    aw = __builtin_fmaf(kr[r], x[r][c], aw);
+                    if (t == p) az = __builtin_fmaf(qr[r], x[r][c], az);
+                }
+                pw[j] = aw;
+                pz[j] = az;
+            }
+            red_w[rg][cb * 4 + c4] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+            if (t == p) red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
+        }
+        __syncthreads();
+        {
+            const float *rw = reinterpret_cast<const float *>(red_w);
+            float w = 0.f;
+#pragma unroll
+            for (int g = 0; g < 16; ++g) w += rw[g * DV + tid];
+            const float bd = bt * (vp - w);
+            if (t == p) {
+                const float *rz = reinterpret_cast<const float *>(red_z);
+                float zz = 0.f;
+#pragma unroll
+                for (int g = 0; g < 16; ++g) zz += rz[g * DV + tid];
+                const float qk = s_qk[0] + s_qk[1];
+                __builtin_nontemporal_store(c_t * __builtin_fmaf(qk, bd, zz),
+                                            o + (size_t)uu * DV + tid);
+            }
+            s_bd[tid] = bd;
+        }
+        __syncthreads();
+        float bdc[COLS_PER_THREAD];
+#pragma unroll
+        for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb * 16 + c];
+#pragma unroll
+        for (int r = 0; r < ROWS_PER_THREAD; ++r)
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c)
+                x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
+    }
+
+    // ---- requantize the window-end state into the pool ----
+    {
+        uint32_t hw[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) hw[c] = pack_f16x2(x[0][2 * c], x[0][2 * c + 1]);
+        buf_store16_cached(st, U4{hw[0], hw[1], hw[2], hw[3]}, off_hi, 0);
+        buf_store16_cached(st, U4{hw[4], hw[5], hw[6], hw[7]}, off_hi + 16, 0);
+    }
+#pragma unroll
+    for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(x[r][c]));
+        amax = pair_max(amax);
+        const float s = group_scale(amax);
+        const double rinv = pack_reciprocal(s);
+        U4 cw;
+        cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
+        cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
+        cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
+        cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
+        buf_store16(st, cw, off_lo, LO_OFF + 2048 * (r - 1));
+        if ((cb & 1) == 0) buf_storef(st, s, off_sc + 256 * (r - 1), SC_OFF);
+    }
+}
+
+hipError_t launch_window(int kind, const PoolView &pool, uint8_t *buf, int window,
+                         const int32_t *slots, const int32_t *pos, int n, const float *q,
+                         const float *k, const float *v, const float *gate, const float *beta,
+                         float *o, hipStream_t stream) {
+    dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
+    const size_t lds = (size_t)window * window_record_bytes(kind);
+    if (kind == 0)
+        hipLaunchKernelGGL(window_kernel<0>, grid, block, lds, stream, pool, buf, window, slots,
+                           pos, q, k, v, gate, beta, o);
+    else
+        hipLaunchKernelGGL(window_kernel<1>, grid, block, lds, stream, pool, buf, window, slots,
+                           pos, q, k, v, gate, beta, o);
+    return hipGetLastError();
+}
+
+}  // namespace qrs
