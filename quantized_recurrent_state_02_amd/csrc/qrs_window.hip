@@ -33,10 +33,30 @@ __host__ __device__ constexpr int window_record_bytes(int kind) { return kind ==
 
 namespace {
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+// DPP move of v from the lane that CTRL names (all named lanes are in range).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, the same value in every lane.  Four DPP
+// adds (quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors)
+// leave every lane with its 16-lane row sum; each step adds a lane and its
+// partner in both orders, so by commutativity all lanes of a row hold the
+// same bits.  The four row sums are then read through scalar registers.  A
+// butterfly of shuffles would take six LDS-unit permutes instead, each with
+// the latency of an LDS access.
+__device__ __forceinline__ float wave_allsum(float x) {
+    x += dpp_f<0xb1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4e>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    x += dpp_f<0x140>(x);  // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Fields of a record staged in LDS (the record layout, byte offsets).
@@ -56,9 +76,13 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
     const float *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta,
     float *__restrict__ o) {
     constexpr int R = window_record_bytes(KIND);
+    constexpr int BOFF = KIND == 0 ? 512 : 1024;  // beta's byte offset in a record
+    // 16-byte pieces of the earlier records that one thread stages (at most
+    // WIN_MAX - 1 records precede a token)
+    constexpr int NCH = ((WIN_MAX - 1) * (R / 16) + THREADS - 1) / THREADS;
     __shared__ float s_kc[DK];     // current token's k (FP16-rounded), model order
     __shared__ float s_q[DK];      // q, model order
-    __shared__ float s_lam[DK];    // KDA: exp(g) of the token being processed, model order
+    __shared__ float s_lam[DK];    // KDA: exp(g) of the current token, model order
     __shared__ int s_perm[DK];
     __shared__ float s_x0[DK];     // back-propagated query, stored order
     __shared__ float s_coef[WIN_MAX];
@@ -84,13 +108,30 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
     const int rg = tid >> 3;
     const __amdgpu_buffer_rsrc_t st =
         make_rsrc(pool.base + ((size_t)slot * H + h) * UNIT_BYTES, UNIT_BYTES);
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(buf + ((size_t)slot * H + h) * (size_t)window * R, window * R);
+    uint8_t *const recs = buf + ((size_t)slot * H + h) * (size_t)window * R;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(recs, window * R);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs, p * R);  // the p earlier records only
     const int off_hi = HI_OFF + rg * (DV * 2) + cb * 32;
     const int off_lo = rg * DV + cb * 16;
     const int off_sc = (rg * NGRP + (cb >> 1)) * 4;
 
-    // ---- the window-start state ----
+    // ---- loads, in the order their results are needed.  All of a thread's
+    //      record pieces are issued before any is used (reads past the p
+    //      earlier records return zero and touch no memory); the
+    //      window-start state is issued last and stays in flight while wave 0
+    //      back-propagates the query ----
+    U4 part[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) part[i] = buf_load16(rr, 16 * (tid + THREADS * i), 0);
+    const size_t ob = (size_t)uu * DK;
+    const float k_in = k[ob + tid];
+    const float v_in = v[ob + tid];
+    const float q_in = q[ob + tid];
+    const float c_t = pool.smooth[h * DV + tid];
+    const int perm_t = pool.perm[h * DK + tid];
+    const float beta_c = beta[uu];
+    const float alpha_c = KIND == 0 ? gate[uu] : 0.f;
+    const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
     U4 hi_raw[2];
     U4 lo_raw[ROWS_PER_THREAD - 1];
     float sc_old[ROWS_PER_THREAD - 1];
@@ -101,36 +142,102 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
         lo_raw[r - 1] = buf_load16(st, off_lo, LO_OFF + 2048 * (r - 1));
         sc_old[r - 1] = buf_loadf(st, off_sc + 256 * (r - 1), SC_OFF);
     }
-
-    // ---- this window's earlier records (p * R bytes) into LDS, 16 B per lane ----
-    for (int e = tid; e < p * (R / 16); e += THREADS)
-        *reinterpret_cast<U4 *>(s_rec + 16 * e) = buf_load16(rb, 16 * e, 0);
+    const int nrec = p * (R / 16);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int e = tid + THREADS * i;
+        if (e < nrec) *reinterpret_cast<U4 *>(s_rec + 16 * e) = part[i];
+    }
 
     // ---- the current token: FP16 k and v, recorded unless it ends the window ----
-    const size_t ob = (size_t)uu * DK;
-    const uint32_t k16 = f32_to_f16_bits(k[ob + tid]);
-    const uint32_t v16 = f32_to_f16_bits(v[ob + tid]);
-    const float c_t = pool.smooth[h * DV + tid];
-    const float beta_c = beta[uu];
-    const float alpha_c = KIND == 0 ? gate[uu] : 0.f;
-    const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
+    const uint32_t k16 = f32_to_f16_bits(k_in);
+    const uint32_t v16 = f32_to_f16_bits(v_in);
     if (!boundary) {
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k16, rb, p * R + 2 * tid, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v16, rb, p * R + 256 + 2 * tid, 0, 0);
         if (KIND == 1) buf_storef(rb, g_c, p * R + 512 + 4 * tid, 0);
         if (tid == 0) {
-            buf_storef(rb, beta_c, p * R + (KIND == 0 ? 512 : 1024), 0);
+            buf_storef(rb, beta_c, p * R + BOFF, 0);
             if (KIND == 0) buf_storef(rb, alpha_c, p * R + 516, 0);
         }
     }
     s_kc[tid] = f16_bits_to_f32(k16);
-    s_q[tid] = q[ob + tid];
-    s_perm[tid] = pool.perm[h * DK + tid];
+    s_q[tid] = q_in;
+    s_perm[tid] = perm_t;
     if (KIND == 1) s_lam[tid] = expf(g_c);
-    const float vc = f16_bits_to_f32(v16) / c_t;  // v' of the current token, column tid
     __syncthreads();
 
+    if (!boundary) {
+        // ---- wave 0: back-propagate the query through tokens p, p-1, ..., 0;
+        //      the next token's fields are read from LDS ahead of each sum ----
+        if (tid < 64) {
+            const int i0 = tid, i1 = tid + 64;  // stored rows of this lane
+            const int m0 = s_perm[i0], m1 = s_perm[i1];
+            float x0 = s_q[m0], x1 = s_q[m1];
+            float ka = s_kc[m0], kb = s_kc[m1], bt = beta_c;
+            float la = KIND == 0 ? alpha_c : s_lam[m0];
+            float lb = KIND == 0 ? alpha_c : s_lam[m1];
+            for (int t = p; t >= 0; --t) {
+                // token t - 1 (record 0 again at t = 0, where it goes unused)
+                const uint8_t *rec = s_rec + (t > 0 ? t - 1 : 0) * R;
+                const float nka = lds_f16(rec, 2 * m0), nkb = lds_f16(rec, 2 * m1);
+                const float nbt = lds_f32(rec, BOFF);
+                const float nla = KIND == 0 ? lds_f32(rec, 516) : lds_f32(rec, 512 + 4 * m0);
+                const float nlb = KIND == 0 ? nla : lds_f32(rec, 512 + 4 * m1);
+                const float coef = bt * wave_allsum(__builtin_fmaf(ka, x0, kb * x1));
+                if (tid == 0) s_coef[t] = coef;
+                x0 = la * (x0 - coef * ka);
+                x1 = lb * (x1 - coef * kb);
+                ka = nka;
+                kb = nkb;
+                bt = nbt;
+                la = KIND == 0 ? nla : expf(nla);
+                lb = KIND == 0 ? nlb : expf(nlb);
+            }
+            s_x0[i0] = x0;
+            s_x0[i1] = x1;
+        }
+        __syncthreads();
+        // ---- z = S_0^T x_0 straight from the packed rows: FP16 rows as
+        //      x_0 * f32(h), INT8 rows as (x_0 s) * code ----
+        float xr0 = s_x0[rg];
+        float xs[ROWS_PER_THREAD - 1];
+#pragma unroll
+        for (int r = 1; r < ROWS_PER_THREAD; ++r) xs[r - 1] = s_x0[rg + 16 * r] * sc_old[r - 1];
+        const uint32_t hw[8] = {hi_raw[0].x, hi_raw[0].y, hi_raw[0].z, hi_raw[0].w,
+                                hi_raw[1].x, hi_raw[1].y, hi_raw[1].z, hi_raw[1].w};
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            float pz[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 4 * c4 + j;
+                float az = (c & 1) ? mul_f16hi(xr0, hw[c >> 1]) : mul_f16lo(xr0, hw[c >> 1]);
+#pragma unroll
+                for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+                    const uint32_t lw[4] = {lo_raw[r - 1].x, lo_raw[r - 1].y, lo_raw[r - 1].z,
+                                            lo_raw[r - 1].w};
+                    az = __builtin_fmaf(xs[r - 1], sext_byte_to_f32(lw[c >> 2], c & 3), az);
+                }
+                pz[j] = az;
+            }
+            red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
+        }
+        __syncthreads();
+        const float *rz = reinterpret_cast<const float *>(red_z);
+        float z = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) z += rz[g * DV + tid];
+        // the buffered writes: o = c z + sum_t coef_t v_t, since v'_t = v_t / c
+        float acc = s_coef[p] * f16_bits_to_f32(v16);
+        for (int t = 0; t < p; ++t)
+            acc = __builtin_fmaf(s_coef[t], lds_f16(s_rec + t * R, 256 + 2 * tid), acc);
+        __builtin_nontemporal_store(__builtin_fmaf(c_t, z, acc), o + (size_t)uu * DV + tid);
+        return;
+    }
+
     // ---- dequantize (no decay: decays come with each token) ----
+    const float vc = f16_bits_to_f32(v16) / c_t;  // v' of the current token, column tid
     float x[ROWS_PER_THREAD][COLS_PER_THREAD];
     {
         const uint32_t hw[8] = {hi_raw[0].x, hi_raw[0].y, hi_raw[0].z, hi_raw[0].w,
@@ -149,74 +256,9 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
         for (int c = 0; c < 16; ++c) x[r][c] = sc_old[r - 1] * sext_byte_to_f32(lw[c >> 2], c & 3);
     }
 
-    if (!boundary) {
-        // ---- wave 0: back-propagate the query through tokens p, p-1, ..., 0 ----
-        if (tid < 64) {
-            const int i0 = tid, i1 = tid + 64;  // stored rows of this lane
-            const int m0 = s_perm[i0], m1 = s_perm[i1];
-            float x0 = s_q[m0], x1 = s_q[m1];
-            for (int t = p; t >= 0; --t) {
-                float ka, kb, la, lb, bt;
-                if (t == p) {
-                    ka = s_kc[m0];
-                    kb = s_kc[m1];
-                    bt = beta_c;
-                    la = KIND == 0 ? alpha_c : s_lam[m0];
-                    lb = KIND == 0 ? alpha_c : s_lam[m1];
-                } else {
-                    const uint8_t *rec = s_rec + t * R;
-                    ka = lds_f16(rec, 2 * m0);
-                    kb = lds_f16(rec, 2 * m1);
-                    bt = lds_f32(rec, KIND == 0 ? 512 : 1024);
-                    if (KIND == 0) {
-                        la = lb = lds_f32(rec, 516);
-                    } else {
-                        la = expf(lds_f32(rec, 512 + 4 * m0));
-                        lb = expf(lds_f32(rec, 512 + 4 * m1));
-                    }
-                }
-                const float coef = bt * wave_sum(__builtin_fmaf(ka, x0, kb * x1));
-                if (tid == 0) s_coef[t] = coef;
-                x0 = la * (x0 - coef * ka);
-                x1 = lb * (x1 - coef * kb);
-            }
-            s_x0[i0] = x0;
-            s_x0[i1] = x1;
-        }
-        __syncthreads();
-        // ---- z = S_0^T x_0 ----
-        float xr[ROWS_PER_THREAD];
-#pragma unroll
-        for (int r = 0; r < ROWS_PER_THREAD; ++r) xr[r] = s_x0[rg + 16 * r];
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            float pz[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 4 * c4 + j;
-                float az = xr[0] * x[0][c];
-#pragma unroll
-                for (int r = 1; r < ROWS_PER_THREAD; ++r) az = __builtin_fmaf(xr[r], x[r][c], az);
-                pz[j] = az;
-            }
-            red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
-        }
-        __syncthreads();
-        const float *rz = reinterpret_cast<const float *>(red_z);
-        float z = 0.f;
-#pragma unroll
-        for (int g = 0; g < 16; ++g) z += rz[g * DV + tid];
-        // the buffered writes: sum_t v'_t coef_t (column tid)
-        float acc = s_coef[p] * vc;
-        for (int t = 0; t < p; ++t)
-            acc = __builtin_fmaf(s_coef[t], lds_f16(s_rec + t * R, 256 + 2 * tid) / c_t, acc);
-        __builtin_nontemporal_store(c_t * (z + acc), o + (size_t)uu * DV + tid);
-        return;
-    }
-
     // ---- the window's last token: replay tokens 0..p on the state ----
     {
-        const float pqk = wave_sum(s_q[tid] * f16_bits_to_f32(k16));
+        const float pqk = wave_allsum(s_q[tid] * f16_bits_to_f32(k16));
         if ((tid & 63) == 0) s_qk[tid >> 6] = pqk;
     }
     for (int t = 0; t <= p; ++t) {
@@ -224,7 +266,7 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
         if (t < p) {
             const uint8_t *rec = s_rec + t * R;
             vp = lds_f16(rec, 256 + 2 * tid) / c_t;
-            bt = lds_f32(rec, KIND == 0 ? 512 : 1024);
+            bt = lds_f32(rec, BOFF);
             const float at = KIND == 0 ? lds_f32(rec, 516) : 0.f;
 #pragma unroll
             for (int r = 0; r < ROWS_PER_THREAD; ++r) {
