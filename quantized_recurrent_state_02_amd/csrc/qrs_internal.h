@@ -73,6 +73,49 @@ __device__ __forceinline__ float pair_max(float a) {
     return __builtin_bit_cast(float, d);
 }
 
+// v from the lane that the DPP control CTRL names (all controls used here
+// name lanes inside the same 16-lane row, so every source lane exists).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16 r .. 16 r + 15), in every
+// lane of the row: quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and
+// row mirrors.  Each step adds a lane and its partner in both orders, so by
+// commutativity all lanes of a row hold the same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xb1>(x);
+    x += dpp_f<0x4e>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
+    return x;
+}
+
+// The same reduction for a maximum.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xb1>(x));
+    x = fmaxf(x, dpp_f<0x4e>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return x;
+}
+
+// Sum over the 64 lanes of a wave, the same value in every lane: the row
+// sums, then the four rows' sums read through scalar registers.  (A
+// butterfly of shuffles takes six LDS-unit permutes, each with the latency
+// of an LDS access.)
+__device__ __forceinline__ float wave_allsum(float x) {
+    x = row16_sum(x);
+    const int xi = __builtin_bit_cast(int, x);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 // Scale of a group: RN32(amax / 127).  Evaluated as RN32(RN64(amax * RN64(1/127))):
 // the FP64 product is within 2^-52 relative of amax/127, while a quotient of
 // two FP32 numbers is never within 2^-49 relative of an FP32 rounding

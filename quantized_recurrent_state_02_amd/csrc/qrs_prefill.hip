@@ -30,9 +30,10 @@
 // each 16x16 tile).  That layout feeds the next contraction's B operand
 // directly when the contraction index inside each 16-block is taken in the
 // order 4 (l >> 4) + j at step j.  Every contraction runs on FP32 MFMA; the
-// unit lower triangular solve goes block by block (16 tokens): a
-// column-parallel substitution on the VALU inside each diagonal block and
-// MFMA updates of the later blocks.  At
+// unit lower triangular solve goes block by block (16 tokens): the four
+// diagonal blocks are inverted by forward substitution (one lane per column,
+// all four blocks at once), then each wave applies the inverses and the
+// updates of the later blocks to its columns on the matrix cores.  At
 // each chunk end the state is requantized through an LDS copy of the packed
 // unit, stored with 16-byte writes, and dequantized back into registers (the
 // same values a reload of the stored unit gives).
@@ -48,6 +49,7 @@ constexpr int PT = 256;     // threads per workgroup
 constexpr int CT = 64;      // tokens per tile (chunks <= 64 are zero-padded)
 constexpr int LDK = 132;    // row stride (floats) of the [64][128] LDS tiles
 constexpr int LDM = 68;     // row stride of the [64][64] Gram tile
+constexpr int LDI = 20;     // row stride of the inverted diagonal blocks
 
 struct PrefillSmem {
     float K[CT * LDK];   // k' (stored key order)
@@ -60,6 +62,8 @@ struct PrefillSmem {
     float gam[CT];       // g_t
     float rc[CT];        // r(C, t): decay from token t to the chunk end
     float bet[CT];
+    int inv[DK];         // stored row of each model key channel (inverse of pi)
+    float Dinv[CT * LDI];  // block d, row t, column j at (16 d + t) LDI + j: (I + B M)_dd^-1 B_d
 };
 static_assert(sizeof(PrefillSmem) <= 160 * 1024, "fits the 160 KB LDS of a gfx950 CU");
 
@@ -144,9 +148,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         return;
     }
     uint8_t *unit = pool.base + ((size_t)slot * H + h) * unit_bytes;
-    const int in_col = tid & (DK - 1);                      // column this thread loads
-    const int perm_col = pool.perm[h * DK + in_col];        // model key channel of stored row in_col
-    const float c_in = pool.smooth[h * DV + in_col];
+    const int in_col = tid & (DK - 1);  // column this thread owns in the LDS-only phases
+    if (tid < DK) s.inv[pool.perm[h * DK + tid]] = tid;
+    __syncthreads();
     float c_out[2];
     c_out[0] = pool.smooth[h * DV + 32 * w + l16];
     c_out[1] = pool.smooth[h * DV + 32 * w + 16 + l16];
@@ -201,44 +205,75 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
     }
 
     const int nchunks = (T + chunk - 1) / chunk;
+    // One chunk's inputs in registers, read as 16-byte pieces of token rows
+    // in model order: thread tid holds model columns [lc, lc + VPL) of tokens
+    // lt + RPP j.  pi is applied when k and q are written to LDS (stored row
+    // inv[c] of model channel c), and v is divided by c there.  Wave 0's lane
+    // t also holds alpha and beta of token t.  Each input is read through a
+    // buffer resource that ends at the chunk's last real token, so rows
+    // t >= ceff read as zero (and alpha as 1).
+    constexpr int ESZ = IN_BF16 ? 2 : 4;
+    constexpr int VPL = 16 / ESZ;        // values per 16-byte piece
+    constexpr int LPR = DK / VPL;        // pieces per token row
+    constexpr int RPP = PT / LPR;        // token rows per pass of the workgroup
+    constexpr int NLD = CT / RPP;        // pieces per thread per input
+    const int lc = (tid % LPR) * VPL;
+    const int lt = tid / LPR;
+    int inv_c[VPL];
+    float c_c[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        inv_c[i] = s.inv[lc + i];
+        c_c[i] = pool.smooth[h * DV + lc + i];
+    }
+    U4 kr4[NLD], qr4[NLD], vr4[NLD];
+    float a_in = 1.f, b_in = 0.f;
+    // Part 0: k and the gates; part 1: q; part 2: v.  The parts are issued
+    // at different points of the previous chunk.
+    auto load_part = [&](int ch, int part) {
+        const int t0 = ch * chunk;
+        const int ceff = min(chunk, T - t0);
+        const size_t row0 = ((size_t)b * T + t0) * H + h;         // token t0 of (b, h)
+        const int rstride = H * DK * ESZ;                         // bytes between tokens
+        const int bytes = (ceff - 1) * rstride + DK * ESZ;
+        const void *src = part == 0 ? k : part == 1 ? q : v;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const uint8_t *)src + row0 * DK * ESZ, bytes);
+        U4 *dst = part == 0 ? kr4 : part == 1 ? qr4 : vr4;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) dst[j] = buf_load16(rs, (lt + RPP * j) * rstride + lc * ESZ, 0);
+        if (part == 0 && tid < CT) {
+            const size_t gi = ((size_t)b * T + (t0 + tid)) * H + h;
+            a_in = tid < ceff ? alpha[gi] : 1.f;
+            b_in = tid < ceff ? beta[gi] : 0.f;
+        }
+    };
+    // element i of a 16-byte piece, widened to FP32 (bf16 widens exactly)
+    auto elem = [](const U4 &u, int i) -> float {
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        if (IN_BF16) return __builtin_bit_cast(float, (w4[i >> 1] >> (16 * (i & 1))) << 16);
+        return __builtin_bit_cast(float, w4[i]);
+    };
+    load_part(0, 0);
+    load_part(0, 1);
+    load_part(0, 2);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int t0 = ch * chunk;
         const int ceff = min(chunk, T - t0);
-
-        // ---- 1. chunk operands into LDS.  Each input is read through a buffer
-        //      resource that ends at the chunk's last real token, so rows
-        //      t >= ceff read as zero (and alpha as 1 below); all 96 loads of a
-        //      thread are issued before the first LDS store. ----
-        {
-            constexpr int ESZ = IN_BF16 ? 2 : 4;
-            const size_t row0 = ((size_t)b * T + t0) * H + h;         // token t0 of (b, h)
-            const int rstride = H * DK * ESZ;                         // bytes between tokens
-            const int bytes = (ceff - 1) * rstride + DK * ESZ;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t *)k + row0 * DK * ESZ, bytes);
-            const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint8_t *)q + row0 * DK * ESZ, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t *)v + row0 * DK * ESZ, bytes);
-            const int t_first = tid >> 7;                             // rows t_first + 2 i
-            float kv[CT / 2], qv[CT / 2], vv[CT / 2];
+        // ---- 1. chunk operands into LDS (loaded during the previous chunk) ----
 #pragma unroll
-            for (int i = 0; i < CT / 2; ++i) {
-                const int t = t_first + 2 * i;
-                kv[i] = ld_buf<IN_BF16>(rk, t * rstride + perm_col * ESZ);
-                qv[i] = ld_buf<IN_BF16>(rq, t * rstride + perm_col * ESZ);
-                vv[i] = ld_buf<IN_BF16>(rv, t * rstride + in_col * ESZ);
-            }
+        for (int j = 0; j < NLD; ++j) {
+            const int t = lt + RPP * j;
 #pragma unroll
-            for (int i = 0; i < CT / 2; ++i) {
-                const int t = t_first + 2 * i;
-                s.K[t * LDK + in_col] = kv[i];
-                s.Q[t * LDK + in_col] = qv[i];
-                s.VU[t * LDK + in_col] = vv[i] / c_in;  // v' = D_c^{-1} v
+            for (int i = 0; i < VPL; ++i) {
+                s.K[t * LDK + inv_c[i]] = elem(kr4[j], i);
+                s.Q[t * LDK + inv_c[i]] = elem(qr4[j], i);
+                s.VU[t * LDK + lc + i] = elem(vr4[j], i) / c_c[i];  // v' = D_c^{-1} v
             }
         }
         // ---- 2. decay prefix sums (wave 0: lane = token) ----
         if (tid < CT) {
             const int t = tid;
-            const size_t gi = ((size_t)b * T + (t0 + t)) * H + h;
-            const float a = t < ceff ? alpha[gi] : 1.f;
+            const float a = a_in;
             double la = a > 0.f ? log((double)a) : 0.0;
             int z = a > 0.f ? -1 : t;
 #pragma unroll
@@ -253,7 +288,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             s.lg[t] = la;
             s.zi[t] = z;
             s.gam[t] = z >= 0 ? 0.f : expf((float)la);
-            s.bet[t] = t < ceff ? beta[gi] : 0.f;
+            s.bet[t] = b_in;
         }
         __syncthreads();
         if (tid < CT) {
@@ -269,53 +304,82 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         }
         __syncthreads();
 
-        // ---- 4. (I + B M) X = B R, in place on R = [Gamma K | V] held in
-        //      [W | VU], one 16-token block at a time: a column-parallel
-        //      substitution inside the diagonal block, then MFMA updates of the
-        //      later blocks' right-hand sides ----
-        for (int e = tid; e < CT * DK; e += PT) {
-            const int t = e >> 7;
-            s.W[t * LDK + in_col] = s.gam[t] * s.K[t * LDK + in_col];
+        // ---- 4. (I + B M) [W | U] = B [Gamma K | V].  Wave 0 inverts the four
+        //      unit lower triangular 16x16 diagonal blocks, times B: lane
+        //      16 d + j forward-substitutes column j of D_d = (I + B M)_dd^-1 B_d.
+        //      Then each wave solves its 64 of the 256 right-hand-side columns
+        //      block by block on the matrix cores, in registers:
+        //      X_d = D_d R_d, then R_e -= M_ed X_d for the later blocks e.  The
+        //      accumulator layout of each product is the next one's B operand,
+        //      so the blocks need no barrier. ----
+        if (w == 0) {
+            const int d = lane >> 4, j = lane & 15;
+            const float *Md = s.M + 16 * d * LDM + 16 * d;
+            float y[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < t; ++i) acc = __builtin_fmaf(Md[t * LDM + i], y[i], acc);
+                const float bt = s.bet[16 * d + t];
+                y[t] = t < j ? 0.f : t == j ? bt : -bt * acc;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) s.Dinv[(16 * d + t) * LDI + j] = y[t];
         }
         __syncthreads();
+        {
+            const bool wcols = w < 2;  // waves 0, 1: W = T Gamma K; waves 2, 3: U = T V
+            const int cbase = 64 * (w & 1);
+            float *X = wcols ? s.W : s.VU;
+            const float *src = wcols ? s.K : s.VU;
+            // R[d][ct]: rows 16 d + 4 g + r, column cbase + 16 ct + l16
+            v4f R[4][4];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            {
-                float *X = tid < DK ? s.W : s.VU;
-                float x[16];
+            for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const int row = 16 * bb + t;
-                    float acc = X[row * LDK + in_col];
-                    const float *mrow = s.M + row * LDM + 16 * bb;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * d + 4 * g + r;
+                    const float f = wcols ? s.gam[row] : 1.f;  // Gamma K, or V (times 1, exact)
 #pragma unroll
-                    for (int i = 0; i < t; ++i) acc = __builtin_fmaf(-mrow[i], x[i], acc);
-                    x[t] = s.bet[row] * acc;
-                    X[row * LDK + in_col] = x[t];
+                    for (int ct = 0; ct < 4; ++ct)
+                        R[d][ct][r] = f * src[row * LDK + cbase + 16 * ct + l16];
                 }
-            }
-            __syncthreads();
-            if (bb < 3) {
-                // wave w updates 64 of the 256 right-hand-side columns
-                float *X = w < 2 ? s.W : s.VU;
 #pragma unroll
-                for (int b2 = bb + 1; b2 < 4; ++b2) {
-                    const v4f a = lds4(s.M + (16 * b2 + l16) * LDM + 16 * bb + 4 * g);
+            for (int d = 0; d < 4; ++d) {
+                const v4f a = lds4(s.Dinv + (16 * d + l16) * LDI + 4 * g);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = mfma4(a.x, R[d][ct][0], acc);
+                    acc = mfma4(a.y, R[d][ct][1], acc);
+                    acc = mfma4(a.z, R[d][ct][2], acc);
+                    acc = mfma4(a.w, R[d][ct][3], acc);
+                    R[d][ct] = acc;
+                }
+#pragma unroll
+                for (int e = d + 1; e < 4; ++e) {
+                    const v4f m = lds4(s.M + (16 * e + l16) * LDM + 16 * d + 4 * g);
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
-                        const int col = 64 * (w & 1) + 16 * ct + l16;
                         v4f acc = {0.f, 0.f, 0.f, 0.f};
-                        acc = mfma4(a.x, X[(16 * bb + 4 * g + 0) * LDK + col], acc);
-                        acc = mfma4(a.y, X[(16 * bb + 4 * g + 1) * LDK + col], acc);
-                        acc = mfma4(a.z, X[(16 * bb + 4 * g + 2) * LDK + col], acc);
-                        acc = mfma4(a.w, X[(16 * bb + 4 * g + 3) * LDK + col], acc);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) X[(16 * b2 + 4 * g + r) * LDK + col] -= acc[r];
+                        acc = mfma4(m.x, R[d][ct][0], acc);
+                        acc = mfma4(m.y, R[d][ct][1], acc);
+                        acc = mfma4(m.z, R[d][ct][2], acc);
+                        acc = mfma4(m.w, R[d][ct][3], acc);
+                        R[e][ct] -= acc;
                     }
                 }
-                __syncthreads();
             }
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        X[(16 * d + 4 * g + r) * LDK + cbase + 16 * ct + l16] = R[d][ct][r];
         }
+        __syncthreads();
 
         // ---- 5. A_qk = inclusive-lower decayed Q K^T (reuses s.M) ----
         for (int tile = w; tile < 10; tile += 4) {
@@ -386,7 +450,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             }
         }
 
-        // ---- 8. S_C = g_C S0 + K^T diag(r(C, t)) Delta ----
+        // ---- 8. S_C = g_C S0 + K^T diag(r(C, t)) Delta; the next chunk's
+        //      inputs are loaded meanwhile ----
+        if (ch + 1 < nchunks) load_part(ch + 1, 0);
         {
             const float gc = s.gam[CT - 1];
 #pragma unroll
@@ -421,6 +487,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         __syncthreads();  // every wave is done with s.Q and s.K
 
         // ---- 9. chunk end: store the state, continue from what was stored ----
+        if (ch + 1 < nchunks) load_part(ch + 1, 1);
         if (FMT == 1) {
             uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
 #pragma unroll
@@ -438,11 +505,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                         S[rb][0][r] = f16_bits_to_f32(h0);
                         S[rb][1][r] = f16_bits_to_f32(h1);
                     } else {
-                        // this wave's 32 columns are exactly one 32-value group
-                        float amax = fmaxf(fabsf(v0), fabsf(v1));
-#pragma unroll
-                        for (int off = 1; off < 16; off <<= 1)
-                            amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+                        // this wave's 32 columns are exactly one 32-value group,
+                        // held by the 16 lanes of one DPP row
+                        const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
                         const float sc = group_scale(amax);
                         const double rinv = scale_reciprocal(sc);
                         const float q0 = rintf(quant_quotient(v0, rinv));
@@ -457,9 +522,11 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                     }
                 }
             __syncthreads();
+            if (ch + 1 < nchunks) load_part(ch + 1, 2);
             for (int e = tid; e < UNIT_BYTES / 16; e += PT)
                 reinterpret_cast<U4 *>(unit)[e] = reinterpret_cast<const U4 *>(stg)[e];
         } else {
+            if (ch + 1 < nchunks) load_part(ch + 1, 2);
             float *u = reinterpret_cast<float *>(unit);
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb)

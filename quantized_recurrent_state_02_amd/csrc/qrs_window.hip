@@ -33,32 +33,6 @@ __host__ __device__ constexpr int window_record_bytes(int kind) { return kind ==
 
 namespace {
 
-// DPP move of v from the lane that CTRL names (all named lanes are in range).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the 64 lanes of a wave, the same value in every lane.  Four DPP
-// adds (quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors)
-// leave every lane with its 16-lane row sum; each step adds a lane and its
-// partner in both orders, so by commutativity all lanes of a row hold the
-// same bits.  The four row sums are then read through scalar registers.  A
-// butterfly of shuffles would take six LDS-unit permutes instead, each with
-// the latency of an LDS access.
-__device__ __forceinline__ float wave_allsum(float x) {
-    x += dpp_f<0xb1>(x);   // quad_perm [1,0,3,2]
-    x += dpp_f<0x4e>(x);   // quad_perm [2,3,0,1]
-    x += dpp_f<0x141>(x);  // row_half_mirror
-    x += dpp_f<0x140>(x);  // row_mirror
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
 // Fields of a record staged in LDS (the record layout, byte offsets).
 __device__ __forceinline__ float lds_f16(const uint8_t *base, int byte_off) {
     return f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(base + byte_off));
