@@ -251,14 +251,20 @@ BYTES_GDN_WINDOW = (20224 + 20224 / WINDOW + 528 * (WINDOW - 1) / 2 + 528 * (WIN
                     + 3 * 512 + 8)
 
 
-def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph, reps=16):
-    """GDN per-window decode at the serving shape, every slot in the same phase,
-    `reps` whole windows timed; returns (seconds per token step, ok)."""
+def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph, reps=16,
+               staggered=False):
+    """GDN per-window decode at the serving shape, `reps` whole windows timed;
+    returns (seconds per token step, ok).  Every slot in the same phase, or
+    (staggered) slot s at position (s + t) mod window at step t, so that each
+    step has slots at every position and 1/window of them end their window."""
     pool = binding.StatePool(binding.FMT_I8F16, n, H, perm, c)
     slots = torch.arange(n, dtype=torch.int32, device="cuda")
     pool.store(slots, torch.from_numpy(inputs.initial_state(1, n, H)).to("cuda"))
     buf = pool.window_buffer("gdn", WINDOW)
-    pos = [torch.full((n,), j, dtype=torch.int32, device="cuda") for j in range(WINDOW)]
+    if staggered:
+        pos = [((torch.arange(n, device="cuda") + j) % WINDOW).to(torch.int32) for j in range(WINDOW)]
+    else:
+        pos = [torch.full((n,), j, dtype=torch.int32, device="cuda") for j in range(WINDOW)]
     out = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
     T = dev_in["q"].shape[0]
 
@@ -465,6 +471,15 @@ def main():
                           "frac_of_peak": n * H * BYTES_GDN_WINDOW / sec_w / 1e9 / PEAK_HBM_GBS,
                           "finite_outputs": ok_w}
             log(f"[bench] gdn per-window (16): {sec_w * 1e6:.2f} us/step ok={ok_w}")
+            sec_s, ok_s = run_window(torch, binding, inputs, gdn_in, perm1, c1, n, H, warmup,
+                                     use_graph, staggered=True)
+            window_res["staggered"] = {
+                "workload": "the same, slot s at position (s + t) mod 16 at step t",
+                "us_per_step": sec_s * 1e6, "updates_per_s": n * H / sec_s,
+                "gbs": n * H * BYTES_GDN_WINDOW / sec_s / 1e9,
+                "frac_of_peak": n * H * BYTES_GDN_WINDOW / sec_s / 1e9 / PEAK_HBM_GBS,
+                "finite_outputs": ok_s}
+            log(f"[bench] gdn per-window (16), staggered phases: {sec_s * 1e6:.2f} us/step ok={ok_s}")
         if args.only in ("v1", "all"):
             secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_U8H16, gdn_in, perm1,
                                   c1, n, H, steps, warmup, args.pools, use_graph)
