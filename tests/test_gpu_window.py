@@ -74,6 +74,50 @@ def test_windows_match_oracle(kind, cfg, window):
         assert ok_hi.all(), f"window {w}: FP16 rows beyond one ulp: {(~ok_hi).sum()}"
 
 
+@pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
+def test_mixed_positions_in_one_call(kind, cfg):
+    """Slots join at different steps, so every call mixes tokens inside their
+    windows with window ends (slot b at position (t - b) mod window).  Each
+    slot's stored bytes are handed to the oracle when its window starts;
+    readouts match to FP32 rounding and every window end passes the
+    one-quantization-step bar."""
+    H, num_slots, window, steps = 3, 9, 5, 22
+    all_slots = np.array([8, 0, 3, 5, 1, 7], np.int32)
+    n = len(all_slots)
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    gp.store(to_dev(all_slots, torch.int32), to_dev(inputs.initial_state(cfg, n, H)))
+    buf = gp.window_buffer(kind, window)
+    wo = oracle.OracleWindowPool(num_slots, H, perm, c, window)
+    kid = 0 if kind == "gdn" else 1
+    gate_key = "alpha" if kind == "gdn" else "g"
+    ends = 0
+    for t in range(steps):
+        active = np.array([b for b in range(n) if b <= t], np.int64)
+        slots = all_slots[active]
+        pos = ((t - active) % window).astype(np.int32)
+        starting = slots[pos == 0]
+        if len(starting):
+            _sync_oracle(wo, gp, starting)
+        d = inputs.step_inputs(cfg, t, n, H, kind)
+        args = [np.ascontiguousarray(d[x][active]) for x in ("q", "k", "v", gate_key, "beta")]
+        og = gp.window_step(kind, window, buf, to_dev(slots, torch.int32), to_dev(pos, torch.int32),
+                            *(to_dev(a) for a in args)).cpu().numpy()
+        oo = wo.step(slots, pos, *args, kid)
+        err = np.abs(og - oo).max() / np.abs(oo).max()
+        assert err <= 1e-5, f"step {t}: readout error {err:.2e}"
+        done = slots[pos == window - 1]
+        if len(done):
+            gu = split_gpu(gp, done)
+            idx = (done[:, None] * H + np.arange(H)[None, :]).ravel()
+            ou = (wo.pool.hi[idx], wo.pool.lo[idx], wo.pool.sc[idx])
+            ok_lo, ok_hi, _, _ = north_star_step_ok(dequant_units(*gu), dequant_units(*ou), gu[2], ou[2])
+            assert ok_lo.all() and ok_hi.all(), f"step {t}: window-end state of slots {done.tolist()}"
+            ends += len(done)
+    assert ends >= 2 * n - 2
+
+
 def test_invalid_position_and_slot():
     H, window = 2, 4
     gp = binding.StatePool(binding.FMT_I8F16, 3, H)
