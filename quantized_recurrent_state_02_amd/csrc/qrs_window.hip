@@ -33,6 +33,8 @@ __host__ __device__ constexpr int window_record_bytes(int kind) { return kind ==
 
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 // Fields of a record staged in LDS (the record layout, byte offsets).
 __device__ __forceinline__ float lds_f16(const uint8_t *base, int byte_off) {
     return f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(base + byte_off));
@@ -212,14 +214,22 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
 
     // ---- dequantize (no decay: decays come with each token) ----
     const float vc = f16_bits_to_f32(v16) / c_t;  // v' of the current token, column tid
-    float x[ROWS_PER_THREAD][COLS_PER_THREAD];
+    // The state as accumulators of v_mfma_f32_4x4x1f32 (16 blocks of 4 lanes;
+    // lane l's element i is A of lane 4 (l / 4) + i times B of lane l): the 4
+    // lanes of a block share the row group rg and hold columns 16 cb + c for
+    // cb = 4 j .. 4 j + 3, so block accumulator X[h][c] of a lane is its own
+    // rows 4 h .. 4 h + 3 at its own column 16 cb + c.  The rank-1 write of a
+    // token is then one 4x4x1 product per accumulator, with A = k at row
+    // rg + 16 (4 h + (cb & 3)) and B = beta delta at the lane's column.
+    v4f X[2][COLS_PER_THREAD];
+#define XV(r, c) X[(r) >> 2][c][(r) & 3]
     {
         const uint32_t hw[8] = {hi_raw[0].x, hi_raw[0].y, hi_raw[0].z, hi_raw[0].w,
                                 hi_raw[1].x, hi_raw[1].y, hi_raw[1].z, hi_raw[1].w};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            x[0][2 * c] = f16_bits_to_f32(hw[c] & 0xffffu);
-            x[0][2 * c + 1] = f16_bits_to_f32(hw[c] >> 16);
+            XV(0, 2 * c) = f16_bits_to_f32(hw[c] & 0xffffu);
+            XV(0, 2 * c + 1) = f16_bits_to_f32(hw[c] >> 16);
         }
     }
 #pragma unroll
@@ -227,7 +237,7 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
         const uint32_t lw[4] = {lo_raw[r - 1].x, lo_raw[r - 1].y, lo_raw[r - 1].z,
                                 lo_raw[r - 1].w};
 #pragma unroll
-        for (int c = 0; c < 16; ++c) x[r][c] = sc_old[r - 1] * sext_byte_to_f32(lw[c >> 2], c & 3);
+        for (int c = 0; c < 16; ++c) XV(r, c) = sc_old[r - 1] * sext_byte_to_f32(lw[c >> 2], c & 3);
     }
 
     // ---- the window's last token: replay tokens 0..p on the state ----
@@ -235,8 +245,15 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
         const float pqk = wave_allsum(s_q[tid] * f16_bits_to_f32(k16));
         if ((tid & 63) == 0) s_qk[tid >> 6] = pqk;
     }
+    const int ma[2] = {s_perm[rg + 16 * (cb & 3)], s_perm[rg + 16 * (4 + (cb & 3))]};
+    // GDN: every row decays by the same alpha, so the state is kept as gam X
+    // with gam the product of the window's alphas so far: a token's decay is
+    // one multiply instead of one per value; w = sum (k gam) X and the write
+    // adds (k / gam) (beta delta).  When gam falls below 2^-60 (a zero alpha
+    // included) it is folded back into X.  KDA decays its rows in place.
+    float gam = 1.f;
     for (int t = 0; t <= p; ++t) {
-        float kr[ROWS_PER_THREAD], dr[ROWS_PER_THREAD], bt, vp;
+        float kr[ROWS_PER_THREAD], dr[ROWS_PER_THREAD], ka[2], bt, vp;
         if (t < p) {
             const uint8_t *rec = s_rec + t * R;
             vp = lds_f16(rec, 256 + 2 * tid) / c_t;
@@ -248,6 +265,8 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
                 kr[r] = lds_f16(rec, 2 * m);
                 dr[r] = KIND == 0 ? at : expf(lds_f32(rec, 512 + 4 * m));
             }
+            ka[0] = lds_f16(rec, 2 * ma[0]);
+            ka[1] = lds_f16(rec, 2 * ma[1]);
         } else {
             vp = vc;
             bt = beta_c;
@@ -257,28 +276,49 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
                 kr[r] = s_kc[m];
                 dr[r] = KIND == 0 ? alpha_c : s_lam[m];
             }
+            ka[0] = s_kc[ma[0]];
+            ka[1] = s_kc[ma[1]];
         }
         float qr[ROWS_PER_THREAD];
         if (t == p) {
 #pragma unroll
             for (int r = 0; r < ROWS_PER_THREAD; ++r) qr[r] = s_q[s_perm[rg + 16 * r]];
         }
+        if (KIND == 0) {
+            gam *= dr[0];
+            if (gam < 0x1p-60f) {  // the same for every thread
 #pragma unroll
-        for (int r = 0; r < ROWS_PER_THREAD; ++r)
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int c = 0; c < COLS_PER_THREAD; ++c) x[r][c] = dr[r] * x[r][c];
+                    for (int c = 0; c < COLS_PER_THREAD; ++c) X[hh][c] *= gam;
+                gam = 1.f;
+            }
+            const float ginv = __builtin_amdgcn_rcpf(gam);
+#pragma unroll
+            for (int r = 0; r < ROWS_PER_THREAD; ++r) {
+                kr[r] *= gam;
+                if (t == p) qr[r] *= gam;
+            }
+            ka[0] *= ginv;
+            ka[1] *= ginv;
+        } else {
+#pragma unroll
+            for (int r = 0; r < ROWS_PER_THREAD; ++r)
+#pragma unroll
+                for (int c = 0; c < COLS_PER_THREAD; ++c) XV(r, c) = dr[r] * XV(r, c);
+        }
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             float pw[4], pz[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int c = 4 * c4 + j;
-                float aw = kr[0] * x[0][c];
-                float az = t == p ? qr[0] * x[0][c] : 0.f;
+                float aw = kr[0] * XV(0, c);
+                float az = t == p ? qr[0] * XV(0, c) : 0.f;
 #pragma unroll
                 for (int r = 1; r < ROWS_PER_THREAD; ++r) {
-                    aw = __builtin_fmaf(kr[r], x[r][c], aw);
-                    if (t == p) az = __builtin_fmaf(qr[r], x[r][c], az);
+                    aw = __builtin_fmaf(kr[r], XV(r, c), aw);
+                    if (t == p) az = __builtin_fmaf(qr[r], XV(r, c), az);
                 }
                 pw[j] = aw;
                 pz[j] = az;
@@ -309,17 +349,23 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
 #pragma unroll
         for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb * 16 + c];
 #pragma unroll
-        for (int r = 0; r < ROWS_PER_THREAD; ++r)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int c = 0; c < COLS_PER_THREAD; ++c)
-                x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
+                X[hh][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(ka[hh], bdc[c], X[hh][c], 0, 0, 0);
+    }
+    if (KIND == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int c = 0; c < COLS_PER_THREAD; ++c) X[hh][c] *= gam;
     }
 
     // ---- requantize the window-end state into the pool ----
     {
         uint32_t hw[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) hw[c] = pack_f16x2(x[0][2 * c], x[0][2 * c + 1]);
+        for (int c = 0; c < 8; ++c) hw[c] = pack_f16x2(XV(0, 2 * c), XV(0, 2 * c + 1));
         buf_store16_cached(st, U4{hw[0], hw[1], hw[2], hw[3]}, off_hi, 0);
         buf_store16_cached(st, U4{hw[4], hw[5], hw[6], hw[7]}, off_hi + 16, 0);
     }
@@ -327,18 +373,19 @@ __global__ __launch_bounds__(THREADS) void window_kernel(
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
         float amax = 0.f;
 #pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(x[r][c]));
+        for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(XV(r, c)));
         amax = pair_max(amax);
         const float s = group_scale(amax);
         const double rinv = pack_reciprocal(s);
         U4 cw;
-        cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
-        cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
-        cw.z = quant4(x[r][8], x[r][9], x[r][10], x[r][11], rinv);
-        cw.w = quant4(x[r][12], x[r][13], x[r][14], x[r][15], rinv);
+        cw.x = quant4(XV(r, 0), XV(r, 1), XV(r, 2), XV(r, 3), rinv);
+        cw.y = quant4(XV(r, 4), XV(r, 5), XV(r, 6), XV(r, 7), rinv);
+        cw.z = quant4(XV(r, 8), XV(r, 9), XV(r, 10), XV(r, 11), rinv);
+        cw.w = quant4(XV(r, 12), XV(r, 13), XV(r, 14), XV(r, 15), rinv);
         buf_store16(st, cw, off_lo, LO_OFF + 2048 * (r - 1));
         if ((cb & 1) == 0) buf_storef(st, s, off_sc + 256 * (r - 1), SC_OFF);
     }
+#undef XV
 }
 
 hipError_t launch_window(int kind, const PoolView &pool, uint8_t *buf, int window,
