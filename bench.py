@@ -288,6 +288,30 @@ def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph,
 SELECT_SEQ, SELECT_T, SELECT_EVERY = 32, 256, 8
 
 
+def run_copy_reference(torch, nbytes, reps=20):
+    """A plain device copy (torch copy_) of nbytes, reading nbytes and writing
+    nbytes: the rate a kernel that reads and writes each byte once can expect
+    on this machine.  Two source/destination pairs alternate, so the working set
+    exceeds the 256 MB Infinity Cache.  Returns (seconds per copy, GB/s)."""
+    bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+             torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(2)]
+    for a, b in bufs:
+        b.copy_(a)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(reps):
+        a, b = bufs[i % 2]
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    secs = start.elapsed_time(end) / 1e3 / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return secs, 2 * nbytes / secs / 1e9
+
+
 def run_select(torch, binding, H, reps=3):
     g = torch.Generator(device="cuda")
     g.manual_seed(1234)
@@ -442,6 +466,7 @@ def main():
     c1 = inputs.smoothing(1, H, True)
     codec_cmp = None
     window_res = None
+    copy_ref = None
     if args.only in ("gdn", "f32", "v1", "bf16", "window", "all"):
         gdn_in = stage_inputs(torch, inputs, 1, "gdn", n, H, total)
         if args.only in ("gdn", "all"):
@@ -450,6 +475,9 @@ def main():
                                       perm1, c1, n, H, steps, warmup, pools, use_graph)
                 res[("gdn", pools)] = (secs, ok)
                 log(f"[bench] gdn pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+            # the same bytes as one decode step, half read and half written
+            copy_ref = run_copy_reference(torch, n * H * BYTES_GDN // 2)
+            log(f"[bench] device copy of the same bytes: {copy_ref[0] * 1e6:.2f} us, {copy_ref[1]:.0f} GB/s")
         if args.only in ("f32", "all"):
             secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_FP32, gdn_in, perm1,
                                   c1, n, H, steps, warmup, 1, use_graph)
@@ -581,6 +609,13 @@ def main():
         detail["codec_comparison"] = codec_cmp
     if window_res:
         detail["window"] = window_res
+    if copy_ref and ("gdn", args.pools) in res:
+        dec = rate(("gdn", args.pools), BYTES_GDN)
+        detail["copy_reference"] = {
+            "what": "torch copy_ of the bytes of one GDN decode step (half read, half written), "
+                    "two buffer pairs alternating",
+            "us": copy_ref[0] * 1e6, "gbs": copy_ref[1],
+            "decode_gbs_over_copy_gbs": dec["gbs"] / copy_ref[1]}
 
     cpu = None
     if not args.no_cpu_baseline:
