@@ -64,6 +64,7 @@ def load():
     lib.orc_u8_store.argtypes = [p, p, p, i, p, p, p, i, p, i]
     lib.orc_u8_dequant.argtypes = [p, p, p, i, p, p, p, i, p, i]
     lib.orc_u8_decode.argtypes = [p, p, p, i, p, p, p, i, i, p, p, p, p, p, p]
+    lib.orc_u8_prefill.argtypes = [p, p, p, i, p, p, p, i, i, i, p, p, p, p, p, p, i]
     lib.orc_unit_bytes.argtypes = []
     lib.orc_unit_bytes.restype = i64
     _lib = lib
@@ -293,6 +294,18 @@ class OracleU8Pool:
         load().orc_u8_decode(_ptr(self.hi), _ptr(self.lo), _ptr(self.meta), self.num_heads,
                              _ptr(self.perm), _ptr(self.c), _ptr(slots), slots.size, kind,
                              _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(o))
+        return o
+
+    def prefill(self, slots, q, k, v, alpha, beta, chunk, init_from_pool):
+        """Chunked prefill with GDN gating on this tier; q,k,v [n][T][H][128]."""
+        slots = _i32(slots)
+        q, k, v, alpha, beta = (_f32(a) for a in (q, k, v, alpha, beta))
+        n, T = q.shape[0], q.shape[1]
+        o = np.empty_like(q)
+        load().orc_u8_prefill(_ptr(self.hi), _ptr(self.lo), _ptr(self.meta), self.num_heads,
+                              _ptr(self.perm), _ptr(self.c), _ptr(slots), n, T, chunk,
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
+                              int(init_from_pool))
         return o
 
 

@@ -611,6 +611,53 @@ void orc_u8_decode(uint16_t *hi, uint8_t *lo, uint16_t *meta, int num_heads, con
     }
 }
 
+/* Chunked prefill on the first revision's low tier, GDN gating: the
+ * recurrence of orc_i8_prefill (FP32 inside a chunk, sequential), with the
+ * chunk-end state written in the INT8+Hadamard format and read back from it
+ * ([DAMP] Appendix A.5 "Prefill path"). */
+void orc_u8_prefill(uint16_t *hi, uint8_t *lo, uint16_t *meta, int num_heads, const int32_t *perm,
+                    const float *c, const int32_t *slots, int n, int Tlen, int chunk,
+                    const float *q, const float *k, const float *v, const float *alpha,
+                    const float *beta, float *o, int init_from_pool)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t uu = 0; uu < (int64_t)n * num_heads; ++uu) {
+        int b = (int)(uu / num_heads), h = (int)(uu % num_heads);
+        int64_t u = (int64_t)slots[b] * num_heads + h;
+        uint16_t *uhi = hi + u * KHI * DV;
+        uint8_t *ulo = lo + u * KLO * DV;
+        uint16_t *umeta = meta + u * KLO * NGRP * 2;
+        float *Tcur = (float *)malloc(sizeof(float) * DK * DV);
+        float *Tnext = (float *)malloc(sizeof(float) * DK * DV);
+        if (init_from_pool)
+            dequant_unit_u8(uhi, ulo, umeta, Tcur);
+        else
+            memset(Tcur, 0, sizeof(float) * DK * DV);
+        for (int t = 0; t < Tlen; ++t) {
+            int64_t tok = ((int64_t)b * Tlen + t) * num_heads + h;     /* [n][Tlen][H] index */
+            float qp[DK], kp[DK], vp[DV], lam[DK];
+            for (int i = 0; i < DK; ++i) {
+                int src = perm[h * DK + i];
+                qp[i] = q[tok * DK + src];
+                kp[i] = k[tok * DK + src];
+                lam[i] = alpha[tok];
+            }
+            for (int j = 0; j < DV; ++j)
+                vp[j] = v[tok * DV + j] / c[h * DV + j];
+            step_unit_f32(Tcur, Tnext, lam, kp, qp, vp, beta[tok], c + h * DV, o + tok * DV);
+            float *tmp = Tcur;
+            Tcur = Tnext;
+            Tnext = tmp;
+            if ((t + 1) % chunk == 0 || t + 1 == Tlen) {
+                store_unit_u8(Tcur, uhi, ulo, umeta);          /* chunk-end write */
+                dequant_unit_u8(uhi, ulo, umeta, Tcur);        /* the next chunk reads it back */
+            }
+        }
+        free(Tcur);
+        free(Tnext);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Key-channel selection: quantization-error energy of each key channel */
 /* ([DAMP] section 4 "Accumulated-error risk", Eq.(8), and Appendix A.2 */

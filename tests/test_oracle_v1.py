@@ -152,3 +152,59 @@ def test_decode_step_composes_codec_and_fp32_step():
     ref.store(slots, dense.T.reshape(n, H, DK, DV), space=1)
     assert np.array_equal(pool.lo, ref.lo) and np.array_equal(pool.meta, ref.meta)
     assert np.array_equal(pool.hi, ref.hi)
+
+
+def _prefill_setup(seed, n=2, H=2, T=7):
+    from quantized_recurrent_state_02_amd import inputs
+    r = np.random.default_rng(seed)
+    perm = np.stack([r.permutation(DK) for _ in range(H)]).astype(np.int32)
+    c = np.exp(r.uniform(-0.69, 0.69, (H, DV))).astype(np.float32)
+    S = r.normal(0, 0.1, (n, H, DK, DV)).astype(np.float32)
+    S[:, :, 3, :] *= 20
+    d = inputs.prefill_inputs(3, n, H, T)
+    return perm, c, S, d
+
+
+def test_prefill_chunk_one_is_decode_steps():
+    """[DAMP] A.5 prefill path on the v1 tier: with chunks of one token the
+    prefill writes and re-reads the stored state after every token, which is
+    T decode steps of the same tier, bit for bit."""
+    n, H, T = 2, 2, 7
+    perm, c, S, d = _prefill_setup(21, n, H, T)
+    slots = np.arange(n, dtype=np.int32)
+    pa = oracle.OracleU8Pool(n, H, perm, c)
+    pb = oracle.OracleU8Pool(n, H, perm, c)
+    pa.store(slots, S)
+    pb.store(slots, S)
+    o = pa.prefill(slots, d["q"], d["k"], d["v"], d["alpha"], d["beta"], 1, True)
+    for t in range(T):
+        ot = pb.decode_step(slots, d["q"][:, t], d["k"][:, t], d["v"][:, t], d["alpha"][:, t],
+                            d["beta"][:, t], 0)
+        assert np.array_equal(o[:, t], ot), f"token {t}"
+    assert np.array_equal(pa.lo, pb.lo) and np.array_equal(pa.meta, pb.meta)
+    assert np.array_equal(pa.hi, pb.hi)
+
+
+def test_prefill_one_chunk_is_the_fp32_recurrence_then_one_store():
+    """One chunk covering all tokens: the outputs are the uncompressed FP32
+    recurrence from the dequantized start, and the pool holds that
+    recurrence's final state stored once in the v1 format; a fresh request
+    (no initial state) starts from zero."""
+    n, H, T = 2, 2, 7
+    perm, c, S, d = _prefill_setup(22, n, H, T)
+    slots = np.arange(n, dtype=np.int32)
+    for init in (True, False):
+        pool = oracle.OracleU8Pool(n, H, perm, c)
+        pool.store(slots, S)
+        start = pool.dequant(slots, space=1) if init else np.zeros((n, H, DK, DV), np.float32)
+        o = pool.prefill(slots, d["q"], d["k"], d["v"], d["alpha"], d["beta"], 64, init)
+        dense = oracle.OracleDensePool(n, H, perm, c)
+        dense.T[:] = start.reshape(n * H, DK, DV)
+        for t in range(T):
+            ot = dense.decode_step(slots, d["q"][:, t], d["k"][:, t], d["v"][:, t],
+                                   d["alpha"][:, t], d["beta"][:, t], 0)
+            assert np.array_equal(o[:, t], ot), f"init {init} token {t}"
+        ref = oracle.OracleU8Pool(n, H, perm, c)
+        ref.store(slots, dense.T.reshape(n, H, DK, DV), space=1)
+        assert np.array_equal(pool.lo, ref.lo) and np.array_equal(pool.meta, ref.meta)
+        assert np.array_equal(pool.hi, ref.hi)
