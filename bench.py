@@ -157,10 +157,12 @@ PREFILL_FLOP_PER_CHUNK_HEAD = 5 * 64 * 64 * 128 + 6 * 64 * 128 * 128
 PEAK_FP32_MFMA_TFLOPS = 157.3
 
 
-def run_prefill(torch, binding, inputs, bf16, reps=3):
+def run_prefill(torch, binding, inputs, bf16, reps=3, fmt=None):
     """Prefill workload: 8 sequences x 32 heads x 4096 tokens in chunks of 64,
-    GDN gating, fresh requests (zero initial state), compressed pool.  Returns
-    (seconds per call, stats dict)."""
+    GDN gating, fresh requests (zero initial state), compressed pool (the
+    INT8 tier unless fmt names another).  Returns (seconds per call, stats
+    dict)."""
+    fmt = binding.FMT_I8F16 if fmt is None else fmt
     wl = inputs.WORKLOADS[3]
     n, H, T = wl.n, wl.heads, wl.steps
     t0 = time.time()
@@ -171,8 +173,7 @@ def run_prefill(torch, binding, inputs, bf16, reps=3):
         dev[key] = torch.from_numpy(d[key]).to("cuda")
     del d
     log(f"[bench] staged prefill inputs ({'bf16' if bf16 else 'fp32'}) in {time.time() - t0:.1f}s")
-    pool = binding.StatePool(binding.FMT_I8F16, n, H, inputs.protected_perm(3, H),
-                             inputs.smoothing(3, H, False))
+    pool = binding.StatePool(fmt, n, H, inputs.protected_perm(3, H), inputs.smoothing(3, H, False))
     slots = torch.arange(n, dtype=torch.int32, device="cuda")
     out = torch.empty((n, T, H, 128), dtype=torch.float32, device="cuda")
 
@@ -204,7 +205,8 @@ def run_prefill(torch, binding, inputs, bf16, reps=3):
                   "hbm_gbs_algorithmic": hbm / secs / 1e9, "flop_per_call": flop,
                   "finite_outputs": ok,
                   "workload": f"prefill {n} x {H} heads x {T} tokens, chunk {PREFILL_CHUNK}, "
-                              f"{'bf16' if bf16 else 'fp32'} q/k/v, zero initial state"}
+                              f"{'bf16' if bf16 else 'fp32'} q/k/v, zero initial state, "
+                              f"{'INT8+Hadamard (v1)' if fmt == binding.FMT_U8H16 else 'INT8'} tier"}
 
 
 def run_codec_compare(torch, binding, inputs, dev_in, perm, c, n, H, steps):
@@ -536,6 +538,9 @@ def main():
             prefill["bf16" if bf16 else "fp32"] = st
             log(f"[bench] prefill {'bf16' if bf16 else 'fp32'}: {secs * 1e3:.3f} ms/call, "
                 f"{st['tflops_fp32_mfma']:.1f} TFLOP/s fp32 mfma")
+        secs, st = run_prefill(torch, binding, inputs, False, fmt=binding.FMT_U8H16)
+        prefill["v1_fp32"] = st
+        log(f"[bench] prefill v1 tier fp32: {secs * 1e3:.3f} ms/call")
 
     select = {}
     if args.only in ("select", "all"):

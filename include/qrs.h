@@ -91,8 +91,8 @@ enum {
  * and read back as x = H_32 (s16 (code - z16)) / sqrt(32).  A zero s16
  * stores s16 = z16 = 0 and codes 0.  Same unit size and offsets as
  * QRS_FMT_I8F16; the 4-byte word of a group holds s16 in bits 0..15 and z16
- * in bits 16..31.  Decode and store/dequant support it; chunked prefill
- * returns QRS_EUNSUPPORTED.
+ * in bits 16..31.  Decode, store/dequant and chunked prefill support it;
+ * the per-window decode step returns QRS_EUNSUPPORTED.
  */
 
 /*
@@ -246,7 +246,8 @@ int qrs_window_decode_step(qrs_pool pool, int kind, int window, void *buffer, si
  *   chunk: 1..64;  init_from_pool: 1 = start from the slot's stored state,
  *   0 = start from zero.
  * All contractions run on FP32 matrix cores.  FP32 pools store the chunk-end
- * state uncompressed (compression disabled).  Out-of-range slot ids leave
+ * state uncompressed (compression disabled); QRS_FMT_U8H16 pools write and
+ * read it back through the block-32 transform.  Out-of-range slot ids leave
  * their state untouched and fill their outputs with NaN.  n = 0 or T = 0 is
  * a no-op.
  */

@@ -304,7 +304,6 @@ int qrs_chunked_prefill(qrs_pool pool, const int32_t *slots, int n, int T, int c
     if (!pool || n < 0 || T < 0 || chunk < 1 || chunk > 64 || (in_dtype != 0 && in_dtype != 1) ||
         (init_from_pool != 0 && init_from_pool != 1))
         return QRS_EINVAL;
-    if (pool->fmt == QRS_FMT_U8H16) return QRS_EUNSUPPORTED;
     if (n == 0 || T == 0) return QRS_OK;
     if (!slots || !q || !k || !v || !alpha || !beta || !o) return QRS_EINVAL;
     if ((size_t)n * (size_t)pool->num_heads > 0x7fffffffu || T > (1 << 24)) return QRS_EINVAL;

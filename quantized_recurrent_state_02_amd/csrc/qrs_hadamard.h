@@ -27,14 +27,18 @@ namespace qrs {
 // RN64(2^-2.5), the correctly rounded 1/sqrt(32).
 constexpr double kInvSqrt32 = 0x1.6a09e667f3bcdp-3;
 
-// FP64 value of the partner lane tid ^ 1 (DPP quad_perm [1,0,3,2] on both halves).
-__device__ __forceinline__ double partner_f64(double v) {
+// An FP64 value moved across lanes by one DPP control (both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0xB1, 0xF, 0xF, true);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
     const uint32_t hi =
-        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0xB1, 0xF, 0xF, true);
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
+
+// FP64 value of the partner lane tid ^ 1 (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ double partner_f64(double v) { return dpp_f64<0xB1>(v); }
 
 // In place: x (this lane's 16 values of a group) -> this lane's 16 outputs of
 // the normalized block-32 transform.  odd = lane parity within the pair.
@@ -61,6 +65,42 @@ __device__ __forceinline__ void hadamard32_pair(float (&x)[16], bool odd) {
     }
 }
 
+// FP64 value of lane l16 ^ (1 << M) of the same 16-lane DPP row (both halves
+// moved).  Bits 0, 1 and 3 are single DPP exchanges (quad_perm [1,0,3,2],
+// [2,3,0,1], row_ror:8); bit 2 takes the rotation by 4 (from lane l16 - 4) on
+// lanes with the bit set and by 12 (from lane l16 + 4) on the others.
+template <int M>
+__device__ __forceinline__ double row_partner_f64(double v, int l16) {
+    if (M == 0) return dpp_f64<0xB1>(v);
+    if (M == 1) return dpp_f64<0x4E>(v);
+    if (M == 3) return dpp_f64<0x128>(v);
+    const double a = dpp_f64<0x124>(v), b = dpp_f64<0x12C>(v);
+    return (l16 & 4) ? a : b;
+}
+
+// The normalized block-32 transform for a group held by the 16 lanes of a
+// DPP row with two values per lane (the prefill kernel's accumulator
+// layout): x0 is group position l16, x1 position 16 + l16.  H_32 = H_2 (x)
+// H_16: H_2 between the two registers, then H_16 over the lane bits, all in
+// FP64; the result is multiplied by RN64(2^-2.5) and rounded once.
+__device__ __forceinline__ void hadamard32_row(float &x0, float &x1, int l16) {
+    double u = (double)x0 + (double)x1, w = (double)x0 - (double)x1;
+#define QRS_BFLY(M)                                                        \
+    {                                                                      \
+        const double pu = row_partner_f64<M>(u, l16), pw = row_partner_f64<M>(w, l16); \
+        const bool up = (l16 >> (M)) & 1;                                  \
+        u = up ? pu - u : u + pu;                                          \
+        w = up ? pw - w : w + pw;                                          \
+    }
+    QRS_BFLY(0)
+    QRS_BFLY(1)
+    QRS_BFLY(2)
+    QRS_BFLY(3)
+#undef QRS_BFLY
+    x0 = (float)(u * kInvSqrt32);
+    x1 = (float)(w * kInvSqrt32);
+}
+
 __device__ __forceinline__ float pair_minf(float a) {
     const float p = __builtin_bit_cast(
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, true));
@@ -74,10 +114,9 @@ __device__ __forceinline__ float pair_maxf(float a) {
 
 // Parameters of one group from its transformed values (Eq.(3), b = 8):
 // s = RN32((max - min) / 255) stored as FP16 (nearest even); z =
-// round(-min / s16) stored as FP16; both used as stored.  lo / hi: this
-// lane's extremes, combined across the pair here.  A zero stored scale
-// (constant group, or below the FP16 range) gives rinv = 0, hence z = 0 and
-// every code 0.
+// round(-min / s16) stored as FP16; both used as stored.  lo / hi: the
+// group's extremes.  A zero stored scale (constant group, or below the FP16
+// range) gives rinv = 0, hence z = 0 and every code 0.
 struct U8Params {
     float sh;      // FP16 scale as FP32
     float zh;      // FP16 zero point as FP32
@@ -85,9 +124,7 @@ struct U8Params {
     uint32_t meta; // s16 | z16 << 16
 };
 
-__device__ __forceinline__ U8Params u8_params(float lo, float hi) {
-    lo = pair_minf(lo);
-    hi = pair_maxf(hi);
+__device__ __forceinline__ U8Params u8_params_group(float lo, float hi) {
     const float d = hi - lo;
     const float s = (float)((double)d * (1.0 / 255.0));  // RN32(d / 255), as in group_scale
     const uint32_t s16 = f32_to_f16_bits(s);
@@ -99,6 +136,11 @@ __device__ __forceinline__ U8Params u8_params(float lo, float hi) {
     p.zh = f16_bits_to_f32(z16);
     p.meta = s16 | (z16 << 16);
     return p;
+}
+
+// The same from a lane pair's extremes (the decode kernels' mapping).
+__device__ __forceinline__ U8Params u8_params(float lo, float hi) {
+    return u8_params_group(pair_minf(lo), pair_maxf(hi));
 }
 
 // Code of one transformed value: round(y / s16) + z16, saturated to [0, 255],

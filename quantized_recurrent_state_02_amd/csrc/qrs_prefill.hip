@@ -36,7 +36,11 @@
 // updates of the later blocks to its columns on the matrix cores.  At
 // each chunk end the state is requantized through an LDS copy of the packed
 // unit, stored with 16-byte writes, and dequantized back into registers (the
-// same values a reload of the stored unit gives).
+// same values a reload of the stored unit gives).  A wave's 32 columns of a
+// row are exactly one 32-value group, held by the 16 lanes of a DPP row (two
+// values per lane), so a group's scale, or the block-32 transform and
+// extremes of the INT8+Hadamard tier, never leave the wave.
+#include "qrs_hadamard.h"
 #include "qrs_internal.h"
 
 namespace qrs {
@@ -116,7 +120,8 @@ __device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, int tb
 
 }  // namespace
 
-// FMT: QRS_FMT_I8F16 (1) or QRS_FMT_FP32 (0) pool; IN_BF16: q, k, v in bf16.
+// FMT: QRS_FMT_FP32 (0), QRS_FMT_I8F16 (1) or QRS_FMT_U8H16 (2) pool; IN_BF16:
+// q, k, v in bf16.
 template <int FMT, int IN_BF16>
 __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_t *__restrict__ slots,
                                                      int T, int chunk, const void *__restrict__ q,
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
     const int b = uu / H;
     const int h = uu - b * H;
     const int slot = slots[b];
-    const size_t unit_bytes = FMT == 1 ? (size_t)UNIT_BYTES : (size_t)F32_UNIT_BYTES;
+    const size_t unit_bytes = FMT != 0 ? (size_t)UNIT_BYTES : (size_t)F32_UNIT_BYTES;
 
     if (slot < 0 || slot >= pool.num_slots) {
         for (int e = tid; e < T * DV; e += PT) {
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) S[rb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
     if (init_from_pool) {
-        if (FMT == 1) {
+        if (FMT != 0) {
             uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
             const __amdgpu_buffer_rsrc_t ru = make_rsrc(unit, UNIT_BYTES);
             U4 part[(UNIT_BYTES / 16 + PT - 1) / PT];
@@ -184,13 +189,32 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                         if (rb == 0) {
                             S[rb][cb][r] = f16_bits_to_f32(
                                 reinterpret_cast<const uint16_t *>(stg + HI_OFF)[row * DV + col]);
-                        } else {
+                        } else if (FMT == 1) {
                             const int lr = row - KHI;
                             const float sc = reinterpret_cast<const float *>(stg + SC_OFF)[lr * NGRP + w];
                             S[rb][cb][r] =
                                 sc * (float)reinterpret_cast<const int8_t *>(stg + LO_OFF)[lr * DV + col];
+                        } else {
+                            // transformed-domain value s16 (code - z16); the
+                            // inverse transform follows once both halves are in
+                            const int lr = row - KHI;
+                            const uint32_t m = reinterpret_cast<const uint32_t *>(stg + SC_OFF)[lr * NGRP + w];
+                            const uint32_t cw = reinterpret_cast<const uint8_t *>(stg + LO_OFF)[lr * DV + col];
+                            S[rb][cb][r] = u8_dequant(cw, 0, f16_bits_to_f32(m & 0xffffu),
+                                                      f16_bits_to_f32(m >> 16));
                         }
                     }
+            if (FMT == 2) {
+#pragma unroll
+                for (int rb = 1; rb < 8; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x0 = S[rb][0][r], x1 = S[rb][1][r];
+                        hadamard32_row(x0, x1, l16);
+                        S[rb][0][r] = x0;
+                        S[rb][1][r] = x1;
+                    }
+            }
             __syncthreads();
         } else {
             const float *u = reinterpret_cast<const float *>(unit);
@@ -488,7 +512,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
 
         // ---- 9. chunk end: store the state, continue from what was stored ----
         if (ch + 1 < nchunks) load_part(ch + 1, 1);
-        if (FMT == 1) {
+        if (FMT != 0) {
             uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb)
@@ -504,9 +528,23 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                         hp[row * DV + c1] = (uint16_t)h1;
                         S[rb][0][r] = f16_bits_to_f32(h0);
                         S[rb][1][r] = f16_bits_to_f32(h1);
+                    } else if (FMT == 2) {
+                        // forward transform, asymmetric UINT8 codes with FP16
+                        // s, z, reconstruction, inverse transform
+                        hadamard32_row(v0, v1, l16);
+                        const U8Params pr = u8_params_group(row16_min(fminf(v0, v1)),
+                                                            row16_max(fmaxf(v0, v1)));
+                        const float q0 = u8_code(v0, pr), q1 = u8_code(v1, pr);
+                        const int lr = row - KHI;
+                        uint8_t *cp = stg + LO_OFF;
+                        cp[lr * DV + c0] = (uint8_t)(int)q0;
+                        cp[lr * DV + c1] = (uint8_t)(int)q1;
+                        if (l16 == 0) reinterpret_cast<uint32_t *>(stg + SC_OFF)[lr * NGRP + w] = pr.meta;
+                        float y0 = pr.sh * (q0 - pr.zh), y1 = pr.sh * (q1 - pr.zh);
+                        hadamard32_row(y0, y1, l16);
+                        S[rb][0][r] = y0;
+                        S[rb][1][r] = y1;
                     } else {
-                        // this wave's 32 columns are exactly one 32-value group,
-                        // held by the 16 lanes of one DPP row
                         const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
                         const float sc = group_scale(amax);
                         const double rinv = scale_reciprocal(sc);
@@ -562,6 +600,8 @@ hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, i
     }
     QRS_PREFILL_CASE(1, 0)
     QRS_PREFILL_CASE(1, 1)
+    QRS_PREFILL_CASE(2, 0)
+    QRS_PREFILL_CASE(2, 1)
     QRS_PREFILL_CASE(0, 0)
     QRS_PREFILL_CASE(0, 1)
 #undef QRS_PREFILL_CASE
