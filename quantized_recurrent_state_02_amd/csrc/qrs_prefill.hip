@@ -40,6 +40,8 @@
 // row are exactly one 32-value group, held by the 16 lanes of a DPP row (two
 // values per lane), so a group's scale, or the block-32 transform and
 // extremes of the INT8+Hadamard tier, never leave the wave.
+#include <cstddef>
+
 #include "qrs_hadamard.h"
 #include "qrs_internal.h"
 
@@ -70,6 +72,9 @@ struct PrefillSmem {
     float Dinv[CT * LDI];  // block d, row t, column j at (16 d + t) LDI + j: (I + B M)_dd^-1 B_d
 };
 static_assert(sizeof(PrefillSmem) <= 160 * 1024, "fits the 160 KB LDS of a gfx950 CU");
+static_assert(offsetof(PrefillSmem, W) == offsetof(PrefillSmem, VU) + sizeof(float) * CT * LDK &&
+                  KLO * LDK <= 2 * CT * LDK,
+              "the chunk-end FP32 rows fit in VU and W");
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -514,6 +519,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         if (ch + 1 < nchunks) load_part(ch + 1, 1);
         if (FMT != 0) {
             uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
+            // FP32 rows 16..127 of the state for the INT8+Hadamard tier's
+            // pass; VU and W (adjacent) are free from here to the next chunk
+            float *F = reinterpret_cast<float *>(smem_raw + offsetof(PrefillSmem, VU));
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
@@ -529,21 +537,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                         S[rb][0][r] = f16_bits_to_f32(h0);
                         S[rb][1][r] = f16_bits_to_f32(h1);
                     } else if (FMT == 2) {
-                        // forward transform, asymmetric UINT8 codes with FP16
-                        // s, z, reconstruction, inverse transform
-                        hadamard32_row(v0, v1, l16);
-                        const U8Params pr = u8_params_group(row16_min(fminf(v0, v1)),
-                                                            row16_max(fmaxf(v0, v1)));
-                        const float q0 = u8_code(v0, pr), q1 = u8_code(v1, pr);
-                        const int lr = row - KHI;
-                        uint8_t *cp = stg + LO_OFF;
-                        cp[lr * DV + c0] = (uint8_t)(int)q0;
-                        cp[lr * DV + c1] = (uint8_t)(int)q1;
-                        if (l16 == 0) reinterpret_cast<uint32_t *>(stg + SC_OFF)[lr * NGRP + w] = pr.meta;
-                        float y0 = pr.sh * (q0 - pr.zh), y1 = pr.sh * (q1 - pr.zh);
-                        hadamard32_row(y0, y1, l16);
-                        S[rb][0][r] = y0;
-                        S[rb][1][r] = y1;
+                        // INT8+Hadamard rows go through LDS (pass below)
+                        F[(row - KHI) * LDK + c0] = v0;
+                        F[(row - KHI) * LDK + c1] = v1;
                     } else {
                         const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
                         const float sc = group_scale(amax);
@@ -560,6 +556,64 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                     }
                 }
             __syncthreads();
+            if (FMT == 2) {
+                // Each 32-value group on a lane pair, 16 values per lane (the
+                // codec's mapping): forward transform, codes and (s16, z16)
+                // into the staged unit, reconstruction, inverse transform.
+                // Task e: group (row KHI + e/2 mod 112, group e/224), half e&1,
+                // so the lanes of a pair are adjacent and consecutive pairs
+                // read consecutive rows (distinct LDS banks).
+                for (int e = tid; e < KLO * NGRP * 2; e += PT) {
+                    const int gi = e >> 1, half = e & 1;
+                    const int lr = gi % KLO, gq = gi / KLO;
+                    float *x = F + lr * LDK + GRP * gq + 16 * half;
+                    float y[16];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const v4f t4 = lds4(x + 4 * j);
+                        y[4 * j] = t4.x;
+                        y[4 * j + 1] = t4.y;
+                        y[4 * j + 2] = t4.z;
+                        y[4 * j + 3] = t4.w;
+                    }
+                    hadamard32_pair(y, half);
+                    float lo = y[0], hi = y[0];
+#pragma unroll
+                    for (int j = 1; j < 16; ++j) {
+                        lo = fminf(lo, y[j]);
+                        hi = fmaxf(hi, y[j]);
+                    }
+                    const U8Params pr = u8_params(lo, hi);
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float q0 = u8_code(y[4 * j], pr), q1 = u8_code(y[4 * j + 1], pr);
+                        const float q2 = u8_code(y[4 * j + 2], pr), q3 = u8_code(y[4 * j + 3], pr);
+                        wd[j] = pack4_u8(q0, q1, q2, q3);
+                        y[4 * j] = pr.sh * (q0 - pr.zh);
+                        y[4 * j + 1] = pr.sh * (q1 - pr.zh);
+                        y[4 * j + 2] = pr.sh * (q2 - pr.zh);
+                        y[4 * j + 3] = pr.sh * (q3 - pr.zh);
+                    }
+                    *reinterpret_cast<U4 *>(stg + LO_OFF + lr * DV + GRP * gq + 16 * half) =
+                        U4{wd[0], wd[1], wd[2], wd[3]};
+                    if (!half) reinterpret_cast<uint32_t *>(stg + SC_OFF)[lr * NGRP + gq] = pr.meta;
+                    hadamard32_pair(y, half);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<v4f *>(x + 4 * j) =
+                            v4f{y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]};
+                }
+                __syncthreads();
+#pragma unroll
+                for (int rb = 1; rb < 8; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int lr = 16 * rb + 4 * g + r - KHI;
+                        S[rb][0][r] = F[lr * LDK + 32 * w + l16];
+                        S[rb][1][r] = F[lr * LDK + 32 * w + 16 + l16];
+                    }
+            }
             if (ch + 1 < nchunks) load_part(ch + 1, 2);
             for (int e = tid; e < UNIT_BYTES / 16; e += PT)
                 reinterpret_cast<U4 *>(unit)[e] = reinterpret_cast<const U4 *>(stg)[e];
