@@ -5,11 +5,14 @@
 // as asymmetric UINT8 codes with an FP16 scale and zero point.  Internal to
 // the library.
 //
-// Thread mapping (the decode / codec kernels): a group's 32 values sit on a
-// lane pair, 16 on the even lane (positions 0..15) and 16 on the odd lane
-// (16..31).  Sylvester's H_32 = H_2 (x) H_16, so each lane applies H_16 to its
-// 16 values in registers and the pair finishes with one butterfly across the
-// lanes, after which each lane holds its own 16 output positions.
+// Thread mapping (the decode and codec kernels, and the prefill kernel's
+// chunk-end pass): a group's 32 values sit on a lane pair, 16 on the even
+// lane (positions 0..15) and 16 on the odd lane (16..31).  Sylvester's
+// H_32 = H_2 (x) H_16, so each lane applies H_16 to its 16 values in
+// registers and the pair finishes with one butterfly across the lanes, after
+// which each lane holds its own 16 output positions.  The prefill kernel's
+// read of the stored state uses a second mapping, a group on the 16 lanes of
+// a DPP row with two values per lane (hadamard32_row).
 //
 // Precision: every butterfly runs in FP64 on FP32 inputs, so the sums are
 // exact whenever the group's nonzero magnitudes span less than 2^24 (29 + 24
@@ -114,9 +117,10 @@ __device__ __forceinline__ float pair_maxf(float a) {
 
 // Parameters of one group from its transformed values (Eq.(3), b = 8):
 // s = RN32((max - min) / 255) stored as FP16 (nearest even); z =
-// round(-min / s16) stored as FP16; both used as stored.  lo / hi: the
-// group's extremes.  A zero stored scale (constant group, or below the FP16
-// range) gives rinv = 0, hence z = 0 and every code 0.
+// round(-min / s16) stored as FP16; both used as stored.  lo / hi: this
+// lane's extremes, combined across the pair here.  A zero stored scale
+// (constant group, or below the FP16 range) gives rinv = 0, hence z = 0 and
+// every code 0.
 struct U8Params {
     float sh;      // FP16 scale as FP32
     float zh;      // FP16 zero point as FP32
@@ -124,7 +128,9 @@ struct U8Params {
     uint32_t meta; // s16 | z16 << 16
 };
 
-__device__ __forceinline__ U8Params u8_params_group(float lo, float hi) {
+__device__ __forceinline__ U8Params u8_params(float lo, float hi) {
+    lo = pair_minf(lo);
+    hi = pair_maxf(hi);
     const float d = hi - lo;
     const float s = (float)((double)d * (1.0 / 255.0));  // RN32(d / 255), as in group_scale
     const uint32_t s16 = f32_to_f16_bits(s);
@@ -136,11 +142,6 @@ __device__ __forceinline__ U8Params u8_params_group(float lo, float hi) {
     p.zh = f16_bits_to_f32(z16);
     p.meta = s16 | (z16 << 16);
     return p;
-}
-
-// The same from a lane pair's extremes (the decode kernels' mapping).
-__device__ __forceinline__ U8Params u8_params(float lo, float hi) {
-    return u8_params_group(pair_minf(lo), pair_maxf(hi));
 }
 
 // Code of one transformed value: round(y / s16) + z16, saturated to [0, 255],

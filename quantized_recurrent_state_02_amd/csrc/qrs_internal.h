@@ -93,20 +93,12 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// The same reduction for a maximum and a minimum.
+// The same reduction for a maximum.
 __device__ __forceinline__ float row16_max(float x) {
     x = fmaxf(x, dpp_f<0xb1>(x));
     x = fmaxf(x, dpp_f<0x4e>(x));
     x = fmaxf(x, dpp_f<0x141>(x));
     x = fmaxf(x, dpp_f<0x140>(x));
-    return x;
-}
-
-__device__ __forceinline__ float row16_min(float x) {
-    x = fminf(x, dpp_f<0xb1>(x));
-    x = fminf(x, dpp_f<0x4e>(x));
-    x = fminf(x, dpp_f<0x141>(x));
-    x = fminf(x, dpp_f<0x140>(x));
     return x;
 }
 
