@@ -23,14 +23,14 @@
 // below).  The VALU work is about 10.6 instructions per state value: convert,
 // scale, two reduction FMAs, the update FMA, half an absmax, a
 // four-instruction exact quantizer whose last step also packs the code byte,
-// and per-row / per-unit overheads.  Four workgroups fit per CU (179 VGPRs);
-// the grid is one workgroup per unit, so the hardware refills CUs as units
-// finish.  On MI355X the step time follows the VALU count (a kernel with a
-// cheaper, inexact quantizer ran 7% faster), while changes to the memory side
-// alone did not move it: workgroups that prefetch a second unit, fewer or
-// more resident workgroups, one wave per column half over a layout with
-// contiguous column halves, and single 16-byte scale accesses all measured
-// the same or slower.
+// and per-row / per-unit overheads.  Six workgroups fit per CU (168 VGPRs,
+// three waves per SIMD); the grid is one workgroup per unit, so the hardware
+// refills CUs as units finish.  On MI355X the step time follows the VALU
+// count (a kernel with a cheaper, inexact quantizer ran 7% faster) and the
+// residency (three waves per SIMD against two: 3-4%), while changes to the
+// memory side alone did not move it: workgroups that prefetch a second unit,
+// one wave per column half over a layout with contiguous column halves, and
+// single 16-byte scale accesses all measured the same or slower.
 #include "qrs_hadamard.h"
 
 namespace qrs {
@@ -53,8 +53,19 @@ __device__ __forceinline__ float wave_sum(float x) {
 // IO 0: q, k, v, o in FP32; IO 1: in bf16 (gates and beta stay FP32).
 // Workgroup i handles slot b = i / hc, head h0 + i % hc; operands and
 // outputs are indexed [n][H] as for the full head range.
+// The INT8 tier is held to 168 VGPRs, three waves per SIMD (six units per
+// CU); at 180 VGPRs it ran two waves per SIMD and was 3-4% slower.  The
+// first revision's tier needs about 200 VGPRs for its transforms and stays
+// at two waves per SIMD.
+template <int CODEC>
+struct DecodeOccupancy {
+    static constexpr int waves = CODEC == 0 ? 3 : 2;
+};
+
 template <int KIND, int CODEC, int IO>
-__global__ __launch_bounds__(THREADS) void decode_packed_kernel(
+__global__ __launch_bounds__(THREADS) __attribute__((
+    amdgpu_waves_per_eu(DecodeOccupancy<CODEC>::waves, DecodeOccupancy<CODEC>::waves))) void
+decode_packed_kernel(
     PoolView pool, const int32_t *__restrict__ slots, int h0, int hc, const void *__restrict__ q,
     const void *__restrict__ k, const void *__restrict__ v, const float *__restrict__ gate,
     const float *__restrict__ beta, void *__restrict__ o) {
@@ -62,6 +73,7 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     __shared__ float s_q[DK];
     __shared__ float s_dec[DK];
     __shared__ float s_bd[DV];
+    __shared__ float s_vp[DV];
     __shared__ float s_qk[2];
     __shared__ float4 red_w[16][DV / 4];
     __shared__ float4 red_z[16][DV / 4];
@@ -113,6 +125,7 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     const float vp_t = ld_stream<IO>(v, ob + tid) / c_t;  // v' = D_c^{-1} v
     const float beta_u = beta[uu];
     s_k[tid] = kt;
+    s_vp[tid] = vp_t;  // read back by this thread after the reductions (one VGPR less)
     s_q[tid] = qt;
     if (KIND == 1) s_dec[tid] = dec_t;
     {
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
             w += rw[g * DV + tid];
             z += rz[g * DV + tid];
         }
-        const float delta = vp_t - w;
+        const float delta = s_vp[tid] - w;
         const float bd = beta_u * delta;
         const float qk = s_qk[0] + s_qk[1];
         st_stream<IO>(o, (size_t)uu * DV + tid, c_t * __builtin_fmaf(qk, bd, z));
@@ -201,9 +214,19 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
     }
     __syncthreads();
 
+    // Re-derive this thread's offsets from an opaque copy of the thread id:
+    // a few integer instructions, where keeping them live across the
+    // reductions made the compiler spill at the 168-VGPR limit.
+    int tid2 = tid;
+    asm volatile("" : "+v"(tid2));
+    const int cb2 = tid2 & 7;
+    const int rg2 = tid2 >> 3;
+    const int off_hi2 = HI_OFF + rg2 * (DV * 2) + cb2 * 32;
+    const int off_lo2 = rg2 * DV + cb2 * 16;
+    const int off_sc2 = (rg2 * NGRP + (cb2 >> 1)) * 4;
     float bdc[COLS_PER_THREAD];
 #pragma unroll
-    for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb * 16 + c];
+    for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb2 * 16 + c];
 
     // ---- rank-1 write, requantize, store: FP16 row (r = 0) ----
     {
@@ -218,8 +241,8 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
         // rows, so these two use the default cache policy and meet in L2;
         // as non-temporal stores the half-filled lines each reached HBM as
         // separate writes (+12% write traffic).
-        buf_store16_cached(st, U4{hw[0], hw[1], hw[2], hw[3]}, off_hi, 0);
-        buf_store16_cached(st, U4{hw[4], hw[5], hw[6], hw[7]}, off_hi + 16, 0);
+        buf_store16_cached(st, U4{hw[0], hw[1], hw[2], hw[3]}, off_hi2, 0);
+        buf_store16_cached(st, U4{hw[4], hw[5], hw[6], hw[7]}, off_hi2 + 16, 0);
     }
     // ---- INT8 rows ----
 #pragma unroll
@@ -245,7 +268,7 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
 #pragma unroll
             for (int c = 0; c < COLS_PER_THREAD; ++c)
                 x[r][c] = __builtin_fmaf(kr[r], bdc[c], x[r][c]);
-            hadamard32_pair(x[r], (cb & 1) != 0);
+            hadamard32_pair(x[r], (cb2 & 1) != 0);
             float lo = x[r][0], hi = x[r][0];
 #pragma unroll
             for (int c = 1; c < COLS_PER_THREAD; ++c) {
@@ -262,8 +285,8 @@ __global__ __launch_bounds__(THREADS) void decode_packed_kernel(
             cw.w = pack4_u8(q[12], q[13], q[14], q[15]);
             meta = __builtin_bit_cast(float, pr.meta);
         }
-        buf_store16(st, cw, off_lo, LO_OFF + 2048 * (r - 1));
-        if ((cb & 1) == 0) buf_storef(st, meta, off_sc + 256 * (r - 1), SC_OFF);
+        buf_store16(st, cw, off_lo2, LO_OFF + 2048 * (r - 1));
+        if ((cb2 & 1) == 0) buf_storef(st, meta, off_sc2 + 256 * (r - 1), SC_OFF);
     }
 }
 
