@@ -35,16 +35,6 @@
 
 namespace qrs {
 
-namespace {
-
-// Sum over the 64 lanes of a wave (every lane gets the total).
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-}  // namespace
 
 // KIND 0: GDN (gate = alpha [n][H]); KIND 1: KDA (gate = g [n][H][128]).
 // CODEC 0: the INT8 tier (symmetric codes, FP32 scale); CODEC 1: the first
@@ -74,6 +64,9 @@ decode_packed_kernel(
     __shared__ float s_dec[DK];
     __shared__ float s_bd[DV];
     __shared__ float s_vp[DV];
+    __shared__ float s_kraw[DK];
+    __shared__ float s_qraw[DK];
+    __shared__ float s_graw[DK];
     __shared__ float s_qk[2];
     __shared__ float4 red_w[16][DV / 4];
     __shared__ float4 red_z[16][DV / 4];
@@ -99,7 +92,23 @@ decode_packed_kernel(
     const int off_lo = rg * DV + cb * 16;
     const int off_sc = (rg * NGRP + (cb >> 1)) * 4;
 
-    // ---- issue the state loads first (the long-latency part) ----
+    // ---- operand loads: thread t loads element t of k, q (KDA: g) and v in
+    //      model order, pi[h][t] and c[h][t].  None depends on another, so
+    //      they and the state loads behind them leave at once; the gather
+    //      through pi runs in LDS afterwards.  (A gather from global memory
+    //      needs pi first, and with one in-order load counter that wait would
+    //      hold back the state loads by a full memory round trip.) ----
+    const size_t ob = (size_t)uu * DK;
+    const int src = pool.perm[h * DK + tid];
+    const float k_m = ld_stream<IO>(k, ob + tid);
+    const float q_m = ld_stream<IO>(q, ob + tid);
+    float g_m = 0.f;
+    if (KIND == 1) g_m = __builtin_nontemporal_load(gate + ob + tid);
+    const float c_t = pool.smooth[h * DV + tid];
+    const float v_m = ld_stream<IO>(v, ob + tid);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- state loads (the long-latency part) ----
     U4 hi_raw[2];
     U4 lo_raw[ROWS_PER_THREAD - 1];
     float sc_old[ROWS_PER_THREAD - 1];
@@ -110,26 +119,28 @@ decode_packed_kernel(
         lo_raw[r - 1] = buf_load16(st, off_lo, LO_OFF + 2048 * (r - 1));
         sc_old[r - 1] = buf_loadf(st, off_sc + 256 * (r - 1), SC_OFF);
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- operands: thread t gathers stored row t and owns value column t ----
-    const size_t ob = (size_t)uu * DK;
-    const int src = pool.perm[h * DK + tid];
-    const float kt = ld_gather<IO>(k, ob, src);
-    const float qt = ld_gather<IO>(q, ob, src);
-    float dec_t;
-    if (KIND == 0)
-        dec_t = gate[uu];
-    else
-        dec_t = expf(buf_loadf(make_rsrc(gate + ob, DK * 4), src * 4, 0));
-    const float c_t = pool.smooth[h * DV + tid];
-    const float vp_t = ld_stream<IO>(v, ob + tid) / c_t;  // v' = D_c^{-1} v
+    // ---- gather through pi: thread t takes stored row t ----
     const float beta_u = beta[uu];
+    s_kraw[tid] = k_m;
+    s_qraw[tid] = q_m;
+    if (KIND == 1) s_graw[tid] = g_m;
+    s_vp[tid] = v_m / c_t;  // v' = D_c^{-1} v, read back by this thread after the reductions
+    __syncthreads();
+    const float kt = s_kraw[src];
+    const float qt = s_qraw[src];
     s_k[tid] = kt;
-    s_vp[tid] = vp_t;  // read back by this thread after the reductions (one VGPR less)
     s_q[tid] = qt;
-    if (KIND == 1) s_dec[tid] = dec_t;
+    float dec_t;
+    if (KIND == 0) {
+        dec_t = gate[uu];
+    } else {
+        dec_t = expf(s_graw[src]);
+        s_dec[tid] = dec_t;
+    }
     {
-        const float p = wave_sum(qt * kt);
+        const float p = wave_allsum(qt * kt);
         if ((tid & 63) == 0) s_qk[tid >> 6] = p;
     }
     __syncthreads();
