@@ -56,7 +56,8 @@ template <int KIND, int CODEC, int IO>
 __global__ __launch_bounds__(THREADS) __attribute__((
     amdgpu_waves_per_eu(DecodeOccupancy<CODEC>::waves, DecodeOccupancy<CODEC>::waves))) void
 decode_packed_kernel(
-    PoolView pool, const int32_t *__restrict__ slots, int h0, int hc, const void *__restrict__ q,
+    PoolView pool, const int32_t *__restrict__ slots, int first_gen, int n_cus, int h0, int hc,
+    const void *__restrict__ q,
     const void *__restrict__ k, const void *__restrict__ v, const float *__restrict__ gate,
     const float *__restrict__ beta, void *__restrict__ o) {
     __shared__ float s_k[DK];
@@ -71,6 +72,15 @@ decode_packed_kernel(
     __shared__ float4 red_w[16][DV / 4];
     __shared__ float4 red_z[16][DV / 4];
 
+    // Staggered start of the first generation (the workgroups resident at
+    // launch, first_gen = 0 when the grid is too small to benefit): the
+    // j-th workgroup placed on each CU waits j x ~0.85 us, so the first
+    // workgroups get their state sooner and compute while the others
+    // load, instead of all loading and then all computing at once.
+    if ((int)blockIdx.x < first_gen) {
+        const int j = (int)blockIdx.x / n_cus;
+        for (int i = 0; i < j; ++i) __builtin_amdgcn_s_sleep(32);
+    }
     const int tid = threadIdx.x;
     const int H = pool.num_heads;
     const int b = blockIdx.x / hc;
@@ -302,10 +312,36 @@ decode_packed_kernel(
 }
 
 // Launcher (host): one workgroup per (slot, head) unit of heads [h0, h0 + hc).
+// The number of workgroups resident at launch (occupancy x CUs) is queried
+// once per device and kernel.
+template <int K, int C, int I>
+static void decode_residency(int *per_cu, int *cus) {
+    static int s_per[16], s_cus[16];
+    int dev = 0;
+    *per_cu = 0;
+    *cus = 1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return;
+    if (s_per[dev] == 0) {
+        int p = 0, c = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, decode_packed_kernel<K, C, I>, THREADS,
+                                                         0) != hipSuccess ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            return;
+        s_cus[dev] = c;
+        s_per[dev] = p;
+    }
+    *per_cu = s_per[dev];
+    *cus = s_cus[dev];
+}
+// The stagger pays off only when later generations follow the first.
 #define QRS_DECODE_CASE(K, C, I)                                                                  \
     if (kind == K && codec == C && io == I) {                                                     \
+        int per_cu = 0, cus = 1;                                                                  \
+        decode_residency<K, C, I>(&per_cu, &cus);                                                 \
+        const int first_gen = n * hc > 2 * per_cu * cus ? per_cu * cus : 0;                      \
         hipLaunchKernelGGL((decode_packed_kernel<K, C, I>), grid, block, 0, stream, pool, slots,  \
-                           h0, hc, q, k, v, gate, beta, o);                                       \
+                           first_gen, cus, h0, hc, q, k, v, gate, beta, o);                       \
         return hipGetLastError();                                                                 \
     }
 hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &pool,
