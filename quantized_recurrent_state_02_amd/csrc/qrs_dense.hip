@@ -8,23 +8,25 @@
 
 namespace qrs {
 
-namespace {
-__device__ __forceinline__ float wave_sum_f(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-}  // namespace
-
+// Thread t (cb = t & 7, rg = t >> 3) owns rows rg + 16 r (r = 0..7) and the
+// 16 columns 32 j + 4 cb + i (j, i = 0..3): each 16-byte access of a wave
+// then covers 8 whole 128-byte row segments.  The unit is addressed through
+// a buffer resource (one 32-bit offset per lane), which keeps the kernel at
+// three waves per SIMD.
 template <int KIND>
-__global__ __launch_bounds__(THREADS) void decode_f32_kernel(
-    PoolView pool, const int32_t *__restrict__ slots, int h0, int hc, const float *__restrict__ q,
-    const float *__restrict__ k, const float *__restrict__ v, const float *__restrict__ gate,
-    const float *__restrict__ beta, float *__restrict__ o) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void
+decode_f32_kernel(PoolView pool, const int32_t *__restrict__ slots, int h0, int hc,
+                  const float *__restrict__ q, const float *__restrict__ k,
+                  const float *__restrict__ v, const float *__restrict__ gate,
+                  const float *__restrict__ beta, float *__restrict__ o) {
     __shared__ float s_k[DK];
     __shared__ float s_q[DK];
     __shared__ float s_dec[DK];
     __shared__ float s_bd[DV];
+    __shared__ float s_vp[DV];
+    __shared__ float s_kraw[DK];
+    __shared__ float s_qraw[DK];
+    __shared__ float s_graw[DK];
     __shared__ float s_qk[2];
     __shared__ float4 red_w[16][DV / 4];
     __shared__ float4 red_z[16][DV / 4];
@@ -41,39 +43,54 @@ __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
     }
     const int cb = tid & 7;
     const int rg = tid >> 3;
-    float *unit = reinterpret_cast<float *>(pool.base + ((size_t)slot * H + h) * F32_UNIT_BYTES);
+    const __amdgpu_buffer_rsrc_t st =
+        make_rsrc(pool.base + ((size_t)slot * H + h) * F32_UNIT_BYTES, F32_UNIT_BYTES);
+    const int off = rg * (DV * 4) + cb * 16;  // + 128 j bytes, + 8192 r (row rg + 16 r)
 
+    // operand loads in model order (no load waits on another), then the state
+    const size_t ob = (size_t)uu * DK;
+    const int src = pool.perm[h * DK + tid];
+    const float k_m = __builtin_nontemporal_load(k + ob + tid);
+    const float q_m = __builtin_nontemporal_load(q + ob + tid);
+    float g_m = 0.f;
+    if (KIND == 1) g_m = __builtin_nontemporal_load(gate + ob + tid);
+    const float c_t = pool.smooth[h * DV + tid];
+    const float v_m = __builtin_nontemporal_load(v + ob + tid);
+    __builtin_amdgcn_sched_barrier(0);
     float x[ROWS_PER_THREAD][COLS_PER_THREAD];
 #pragma unroll
     for (int r = 0; r < ROWS_PER_THREAD; ++r) {
-        const float4 *p = reinterpret_cast<const float4 *>(unit + (rg + 16 * r) * DV + cb * 16);
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const float4 t = p[c4];
-            x[r][4 * c4] = t.x;
-            x[r][4 * c4 + 1] = t.y;
-            x[r][4 * c4 + 2] = t.z;
-            x[r][4 * c4 + 3] = t.w;
+        for (int j = 0; j < 4; ++j) {
+            const U4 t = buf_load16(st, off + 128 * j, 8192 * r);
+            x[r][4 * j] = __builtin_bit_cast(float, t.x);
+            x[r][4 * j + 1] = __builtin_bit_cast(float, t.y);
+            x[r][4 * j + 2] = __builtin_bit_cast(float, t.z);
+            x[r][4 * j + 3] = __builtin_bit_cast(float, t.w);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    const size_t ob = (size_t)uu * DK;
-    const int src = pool.perm[h * DK + tid];
-    const float kt = k[ob + src];
-    const float qt = q[ob + src];
-    float dec_t;
-    if (KIND == 0)
-        dec_t = gate[uu];
-    else
-        dec_t = expf(gate[ob + src]);
-    const float c_t = pool.smooth[h * DV + tid];
-    const float vp_t = v[ob + tid] / c_t;
+    // gather through pi in LDS: thread t takes stored row t
     const float beta_u = beta[uu];
+    s_kraw[tid] = k_m;
+    s_qraw[tid] = q_m;
+    if (KIND == 1) s_graw[tid] = g_m;
+    s_vp[tid] = v_m / c_t;
+    __syncthreads();
+    const float kt = s_kraw[src];
+    const float qt = s_qraw[src];
     s_k[tid] = kt;
     s_q[tid] = qt;
-    if (KIND == 1) s_dec[tid] = dec_t;
+    float dec_t;
+    if (KIND == 0) {
+        dec_t = gate[uu];
+    } else {
+        dec_t = expf(s_graw[src]);
+        s_dec[tid] = dec_t;
+    }
     {
-        const float p = wave_sum_f(qt * kt);
+        const float p = wave_allsum(qt * kt);
         if ((tid & 63) == 0) s_qk[tid >> 6] = p;
     }
     __syncthreads();
@@ -86,10 +103,12 @@ __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
 #pragma unroll
         for (int c = 0; c < COLS_PER_THREAD; ++c) x[r][c] *= d;
     }
-    {
-        float pw[COLS_PER_THREAD], pz[COLS_PER_THREAD];
 #pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) {
+    for (int j = 0; j < 4; ++j) {
+        float pw[4], pz[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * j + i;
             float aw = kr[0] * x[0][c];
             float az = s_q[rg] * x[0][c];
 #pragma unroll
@@ -97,16 +116,11 @@ __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
                 aw = __builtin_fmaf(kr[r], x[r][c], aw);
                 az = __builtin_fmaf(s_q[rg + 16 * r], x[r][c], az);
             }
-            pw[c] = aw;
-            pz[c] = az;
+            pw[i] = aw;
+            pz[i] = az;
         }
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            red_w[rg][cb * 4 + c4] =
-                make_float4(pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]);
-            red_z[rg][cb * 4 + c4] =
-                make_float4(pz[4 * c4], pz[4 * c4 + 1], pz[4 * c4 + 2], pz[4 * c4 + 3]);
-        }
+        red_w[rg][8 * j + cb] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+        red_z[rg][8 * j + cb] = make_float4(pz[0], pz[1], pz[2], pz[3]);
     }
     __syncthreads();
     {
@@ -118,26 +132,34 @@ __global__ __launch_bounds__(THREADS) void decode_f32_kernel(
             w += rw[g * DV + tid];
             z += rz[g * DV + tid];
         }
-        const float bd = beta_u * (vp_t - w);
+        const float bd = beta_u * (s_vp[tid] - w);
         const float qk = s_qk[0] + s_qk[1];
-        o[(size_t)uu * DV + tid] = c_t * __builtin_fmaf(qk, bd, z);
+        __builtin_nontemporal_store(c_t * __builtin_fmaf(qk, bd, z), o + (size_t)uu * DV + tid);
         s_bd[tid] = bd;
     }
     __syncthreads();
     float bdc[COLS_PER_THREAD];
 #pragma unroll
-    for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb * 16 + c];
+    for (int j = 0; j < 4; ++j) {
+        const float4 t = reinterpret_cast<const float4 *>(s_bd)[8 * j + cb];
+        bdc[4 * j] = t.x;
+        bdc[4 * j + 1] = t.y;
+        bdc[4 * j + 2] = t.z;
+        bdc[4 * j + 3] = t.w;
+    }
 #pragma unroll
     for (int r = 0; r < ROWS_PER_THREAD; ++r) {
-        float4 *p = reinterpret_cast<float4 *>(unit + (rg + 16 * r) * DV + cb * 16);
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            float4 t;
-            t.x = __builtin_fmaf(kr[r], bdc[4 * c4], x[r][4 * c4]);
-            t.y = __builtin_fmaf(kr[r], bdc[4 * c4 + 1], x[r][4 * c4 + 1]);
-            t.z = __builtin_fmaf(kr[r], bdc[4 * c4 + 2], x[r][4 * c4 + 2]);
-            t.w = __builtin_fmaf(kr[r], bdc[4 * c4 + 3], x[r][4 * c4 + 3]);
-            p[c4] = t;
+        for (int j = 0; j < 4; ++j) {
+            U4 t;
+            t.x = __builtin_bit_cast(uint32_t, __builtin_fmaf(kr[r], bdc[4 * j], x[r][4 * j]));
+            t.y = __builtin_bit_cast(uint32_t,
+                                     __builtin_fmaf(kr[r], bdc[4 * j + 1], x[r][4 * j + 1]));
+            t.z = __builtin_bit_cast(uint32_t,
+                                     __builtin_fmaf(kr[r], bdc[4 * j + 2], x[r][4 * j + 2]));
+            t.w = __builtin_bit_cast(uint32_t,
+                                     __builtin_fmaf(kr[r], bdc[4 * j + 3], x[r][4 * j + 3]));
+            buf_store16(st, t, off + 128 * j, 8192 * r);
         }
     }
 }
