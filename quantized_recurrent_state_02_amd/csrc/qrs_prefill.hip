@@ -15,16 +15,18 @@
 //     delta_t = beta_t (v'_t - g_t S0^T k'_t - sum_{i<t} r(t, i) (k'_i . k'_t) delta_i).
 // In matrix form over the chunk (rows = tokens), with M[t][i] = r(t,i) k'_t.k'_i
 // for i < t:
-//     (I + B M) [W | U] = B [Gamma K | V]        (unit lower triangular)
-//     Delta = U - W S0
+//     (I + B M) Delta = B (V - Gamma K S0)       (unit lower triangular)
 //     O     = Gamma Q S0 + (L o Q K^T) Delta,     L[t][i] = r(t, i) for i <= t
 //     S_C   = g_C S0 + K^T diag(r(C, t)) Delta.
+// (The same Delta as U - W S0 with (I + B M) [W | U] = B [Gamma K | V]; the
+// start state is known when the chunk begins, so the solve needs only the
+// d_v right-hand-side columns of V - Gamma K S0.)
 // Decay ratios are taken from FP64 prefix sums of log(alpha) (a chunk product
 // of alphas underflows FP32); a zero alpha makes every ratio across it zero.
 //
 // Launch: one 256-thread workgroup (four wave64) per (sequence, head); chunks
-// run in order.  Per chunk the waves share K, Q, V/U, W and the two 64x64
-// masked Gram tiles in LDS; wave w owns value columns [32w, 32w + 32) of S0,
+// run in order.  Per chunk the waves share K, Q, V and the two 64x64 masked
+// Gram tiles in LDS; wave w owns value columns [32w, 32w + 32) of S0, Y,
 // Delta and O, which stay in registers in the accumulator layout of
 // v_mfma_f32_16x16x4f32 (lane l holds column l & 15 of rows 4 (l >> 4) + r of
 // each 16x16 tile).  That layout feeds the next contraction's B operand
@@ -61,8 +63,8 @@ struct PrefillSmem {
     float K[CT * LDK];   // k' (stored key order)
     float Q[CT * LDK];   // q'; at chunk end, the packed unit being written
     float VU[CT * LDK];  // v' = v / c, then U = T V in place
-    float W[CT * LDK];   // W = T Gamma K
-    float M[CT * LDM];   // strict-lower decayed K K^T, then inclusive-lower decayed Q K^T
+    float W[CT * LDK];   // A_qk = inclusive-lower decayed Q K^T ([64][LDM]) during a chunk
+    float M[CT * LDM];   // strict-lower decayed K K^T
     double lg[CT];       // prefix sum of log(alpha) over the non-zero alphas
     int zi[CT];          // last token <= t with alpha = 0 (-1 if none)
     float gam[CT];       // g_t
@@ -72,6 +74,7 @@ struct PrefillSmem {
     float Dinv[CT * LDI];  // block d, row t, column j at (16 d + t) LDI + j: (I + B M)_dd^-1 B_d
 };
 static_assert(sizeof(PrefillSmem) <= 160 * 1024, "fits the 160 KB LDS of a gfx950 CU");
+static_assert(CT * LDM <= CT * LDK, "A_qk fits in the W tile");
 static_assert(offsetof(PrefillSmem, W) == offsetof(PrefillSmem, VU) + sizeof(float) * CT * LDK &&
                   KLO * LDK <= 2 * CT * LDK,
               "the chunk-end FP32 rows fit in VU and W");
@@ -101,10 +104,10 @@ __device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, int off) {
 
 // 16x16 tile of the masked Gram matrix  A[t][i] = r(t, i) * (X_t . K_i)  for
 // i < t (STRICT) or i <= t, zero elsewhere, rows t in [16 tb, +16), columns i
-// in [16 sb, +16); X = K or Q from LDS.  Written to s.M.
+// in [16 sb, +16); X = K or Q from LDS.  Written to dst (row stride LDM).
 template <bool STRICT>
-__device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, int tb, int sb, int l16,
-                                          int g) {
+__device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, float *dst, int tb,
+                                          int sb, int l16, int g) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
@@ -119,7 +122,7 @@ __device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, int tb
     for (int r = 0; r < 4; ++r) {
         const int t = 16 * tb + 4 * g + r, i = 16 * sb + l16;
         const bool keep = STRICT ? (i < t) : (i <= t);
-        s.M[t * LDM + i] = keep ? ratio(s, t, i) * acc[r] : 0.f;
+        dst[t * LDM + i] = keep ? ratio(s, t, i) * acc[r] : 0.f;
     }
 }
 
@@ -325,22 +328,48 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             s.rc[t] = t == CT - 1 ? 1.f : ratio(s, CT - 1, t);
         }
 
-        // ---- 3. M = strict-lower decayed K K^T (10 lower tiles over 4 waves) ----
-        for (int tile = w; tile < 10; tile += 4) {
-            const int tb = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
-            const int sb = tile - tb * (tb + 1) / 2;
-            gram_tile<true>(s, s.K, tb, sb, l16, g);
+        // ---- 3. the masked Gram matrices, 20 lower 16x16 tiles over 4 waves:
+        //      M = strict-lower decayed K K^T, A_qk = inclusive-lower decayed
+        //      Q K^T (in the W tile, free during the chunk); then per wave, on
+        //      its 32 value columns, Y = V' - Gamma K S0 in the accumulator
+        //      layout ----
+        float *const Aqk = s.W;
+        for (int tile = w; tile < 20; tile += 4) {
+            const int tt = tile < 10 ? tile : tile - 10;
+            const int tb = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
+            const int sb = tt - tb * (tb + 1) / 2;
+            if (tile < 10)
+                gram_tile<true>(s, s.K, s.M, tb, sb, l16, g);
+            else
+                gram_tile<false>(s, s.Q, Aqk, tb, sb, l16, g);
+        }
+        v4f D[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const v4f a = lds4(s.K + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc0 = mfma4(a[j], S[kb][0][j], acc0);
+                    acc1 = mfma4(a[j], S[kb][1][j], acc1);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * tb + 4 * g + r;
+                const float gm = s.gam[row];
+                const float *u = s.VU + row * LDK + 32 * w + l16;
+                D[tb][0][r] = u[0] - gm * acc0[r];
+                D[tb][1][r] = u[16] - gm * acc1[r];
+            }
         }
         __syncthreads();
 
-        // ---- 4. (I + B M) [W | U] = B [Gamma K | V].  Wave 0 inverts the four
-        //      unit lower triangular 16x16 diagonal blocks, times B: lane
-        //      16 d + j forward-substitutes column j of D_d = (I + B M)_dd^-1 B_d.
-        //      Then each wave solves its 64 of the 256 right-hand-side columns
-        //      block by block on the matrix cores, in registers:
-        //      X_d = D_d R_d, then R_e -= M_ed X_d for the later blocks e.  The
-        //      accumulator layout of each product is the next one's B operand,
-        //      so the blocks need no barrier. ----
+        // ---- 4. Wave 0 inverts the four unit lower triangular 16x16 diagonal
+        //      blocks of I + B M, times B: lane 16 d + j forward-substitutes
+        //      column j of D_d = (I + B M)_dd^-1 B_d. ----
         if (w == 0) {
             const int d = lane >> 4, j = lane & 15;
             const float *Md = s.M + 16 * d * LDM + 16 * d;
@@ -357,90 +386,41 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             for (int t = 0; t < 16; ++t) s.Dinv[(16 * d + t) * LDI + j] = y[t];
         }
         __syncthreads();
-        {
-            const bool wcols = w < 2;  // waves 0, 1: W = T Gamma K; waves 2, 3: U = T V
-            const int cbase = 64 * (w & 1);
-            float *X = wcols ? s.W : s.VU;
-            const float *src = wcols ? s.K : s.VU;
-            // R[d][ct]: rows 16 d + 4 g + r, column cbase + 16 ct + l16
-            v4f R[4][4];
+
+        // ---- 5. per wave: (I + B M) Delta = B Y on its 32 columns, block by
+        //      block on the matrix cores in registers: Delta_d = D_d Y_d, then
+        //      Y_e -= M_ed Delta_d for the later blocks.  This is the Delta of
+        //      (I + B M) [W | U] = B [Gamma K | V], Delta = U - W S0, with half
+        //      the right-hand-side columns; the accumulator layout of each
+        //      product is the next one's B operand. ----
 #pragma unroll
-            for (int d = 0; d < 4; ++d)
+        for (int d = 0; d < 4; ++d) {
+            const v4f a = lds4(s.Dinv + (16 * d + l16) * LDI + 4 * g);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * d + 4 * g + r;
-                    const float f = wcols ? s.gam[row] : 1.f;  // Gamma K, or V (times 1, exact)
+            for (int ct = 0; ct < 2; ++ct) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma4(a.x, D[d][ct][0], acc);
+                acc = mfma4(a.y, D[d][ct][1], acc);
+                acc = mfma4(a.z, D[d][ct][2], acc);
+                acc = mfma4(a.w, D[d][ct][3], acc);
+                D[d][ct] = acc;
+            }
 #pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        R[d][ct][r] = f * src[row * LDK + cbase + 16 * ct + l16];
-                }
+            for (int e = d + 1; e < 4; ++e) {
+                const v4f m = lds4(s.M + (16 * e + l16) * LDM + 16 * d + 4 * g);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const v4f a = lds4(s.Dinv + (16 * d + l16) * LDI + 4 * g);
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
+                for (int ct = 0; ct < 2; ++ct) {
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = mfma4(a.x, R[d][ct][0], acc);
-                    acc = mfma4(a.y, R[d][ct][1], acc);
-                    acc = mfma4(a.z, R[d][ct][2], acc);
-                    acc = mfma4(a.w, R[d][ct][3], acc);
-                    R[d][ct] = acc;
+                    acc = mfma4(m.x, D[d][ct][0], acc);
+                    acc = mfma4(m.y, D[d][ct][1], acc);
+                    acc = mfma4(m.z, D[d][ct][2], acc);
+                    acc = mfma4(m.w, D[d][ct][3], acc);
+                    D[e][ct] -= acc;
                 }
-#pragma unroll
-                for (int e = d + 1; e < 4; ++e) {
-                    const v4f m = lds4(s.M + (16 * e + l16) * LDM + 16 * d + 4 * g);
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        v4f acc = {0.f, 0.f, 0.f, 0.f};
-                        acc = mfma4(m.x, R[d][ct][0], acc);
-                        acc = mfma4(m.y, R[d][ct][1], acc);
-                        acc = mfma4(m.z, R[d][ct][2], acc);
-                        acc = mfma4(m.w, R[d][ct][3], acc);
-                        R[e][ct] -= acc;
-                    }
-                }
-            }
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        X[(16 * d + 4 * g + r) * LDK + cbase + 16 * ct + l16] = R[d][ct][r];
-        }
-        __syncthreads();
-
-        // ---- 5. A_qk = inclusive-lower decayed Q K^T (reuses s.M) ----
-        for (int tile = w; tile < 10; tile += 4) {
-            const int tb = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
-            const int sb = tile - tb * (tb + 1) / 2;
-            gram_tile<false>(s, s.Q, tb, sb, l16, g);
-        }
-        __syncthreads();
-
-        // ---- 6. per wave: Delta = U - W S0 (both column tiles per A read) ----
-        v4f D[4][2];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                const v4f a = lds4(s.W + (16 * tb + l16) * LDK + 16 * kb + 4 * g);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc0 = mfma4(a[j], S[kb][0][j], acc0);
-                    acc1 = mfma4(a[j], S[kb][1][j], acc1);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float *u = s.VU + (16 * tb + 4 * g + r) * LDK + 32 * w + l16;
-                D[tb][0][r] = u[0] - acc0[r];
-                D[tb][1][r] = u[16] - acc1[r];
             }
         }
 
-        // ---- 7. O = Gamma Q S0 + A_qk Delta, written as o = c (.) O ----
+        // ---- 6. O = Gamma Q S0 + A_qk Delta, written as o = c (.) O ----
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -461,7 +441,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             }
 #pragma unroll
             for (int sb = 0; sb <= tb; ++sb) {
-                const v4f a = lds4(s.M + (16 * tb + l16) * LDM + 16 * sb + 4 * g);
+                const v4f a = lds4(Aqk + (16 * tb + l16) * LDM + 16 * sb + 4 * g);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     acc0 = mfma4(a[j], D[sb][0][j], acc0);
@@ -479,7 +459,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             }
         }
 
-        // ---- 8. S_C = g_C S0 + K^T diag(r(C, t)) Delta; the next chunk's
+        // ---- 7. S_C = g_C S0 + K^T diag(r(C, t)) Delta; the next chunk's
         //      inputs are loaded meanwhile ----
         if (ch + 1 < nchunks) load_part(ch + 1, 0);
         {
@@ -515,7 +495,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         }
         __syncthreads();  // every wave is done with s.Q and s.K
 
-        // ---- 9. chunk end: store the state, continue from what was stored ----
+        // ---- 8. chunk end: store the state, continue from what was stored ----
         if (ch + 1 < nchunks) load_part(ch + 1, 1);
         if (FMT != 0) {
             uint8_t *stg = reinterpret_cast<uint8_t *>(s.Q);
