@@ -21,7 +21,8 @@ the 256 MB Infinity Cache and every state read comes from HBM; the
 single-pool figure is reported beside it.
 
 The CPU baseline is the oracle (oracle/, FP32 C code with OpenMP over units)
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload; `detail` also carries the
+oracle's KDA decode and chunked prefill on bounded samples.
 
 `detail` also reports KDA decode, the single-pool variants, the FP32-state
 kernel on the same inputs, and the chunked prefill kernel (8 x 32 heads x
@@ -376,6 +377,26 @@ def cpu_select_baseline(H, samples=192):
             "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))}
 
 
+def cpu_prefill_baseline(inputs, seqs=1, tokens=4096):
+    """The oracle's chunked prefill (sequential FP32 recurrence inside each
+    chunk of 64, compressed chunk ends) on a bounded sample of the prefill
+    workload: `seqs` sequences x 32 heads x `tokens` tokens, zero start."""
+    import oracle
+
+    H = 32
+    d = inputs.prefill_inputs(3, seqs, H, tokens)
+    op = oracle.OraclePool(seqs, H, inputs.protected_perm(3, H), inputs.smoothing(3, H, False))
+    slots = np.arange(seqs, dtype=np.int32)
+    t0 = time.perf_counter()
+    op.prefill(slots, d["q"], d["k"], d["v"], d["alpha"], d["beta"], PREFILL_CHUNK, False)
+    dt = time.perf_counter() - t0
+    return {"tokens_per_s": seqs * tokens / dt, "head_updates_per_s": seqs * tokens * H / dt,
+            "sample": f"{seqs} sequence(s) x {H} heads x {tokens} tokens, chunks of {PREFILL_CHUNK}, "
+                      "zero initial state, INT8 tier",
+            "seconds": dt, "kind": "oracle",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))}
+
+
 def cpu_baseline(inputs, kind, budget_s=12.0):
     """Oracle on a bounded sample of the same workload: all 256 slots x 32
     heads, the first consecutive steps that fit in about `budget_s` seconds
@@ -454,6 +475,7 @@ def main():
     use_graph = not args.no_graph
     units = n * H
     res = {}
+    kda_cpu = None
 
     if args.calib_copy_mb:
         nb = args.calib_copy_mb << 20
@@ -530,6 +552,9 @@ def main():
             res[("kda", pools)] = (secs, ok)
             log(f"[bench] kda pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
         del kda_in
+        if not args.no_cpu_baseline and args.only == "all":
+            kda_cpu = cpu_baseline(inputs, "kda", budget_s=4.0)
+            log(f"[bench] kda cpu oracle: {kda_cpu['value']:.3e} updates/s")
 
     prefill = {}
     if args.only in ("prefill", "all"):
@@ -541,6 +566,9 @@ def main():
         secs, st = run_prefill(torch, binding, inputs, False, fmt=binding.FMT_U8H16)
         prefill["v1_fp32"] = st
         log(f"[bench] prefill v1 tier fp32: {secs * 1e3:.3f} ms/call")
+        if not args.no_cpu_baseline:
+            prefill["cpu_oracle"] = cpu_prefill_baseline(inputs)
+            log(f"[bench] prefill cpu oracle: {prefill['cpu_oracle']['tokens_per_s']:.3e} tokens/s")
 
     select = {}
     if args.only in ("select", "all"):
@@ -614,6 +642,8 @@ def main():
         detail["codec_comparison"] = codec_cmp
     if window_res:
         detail["window"] = window_res
+    if kda_cpu:
+        detail["kda_cpu_oracle"] = kda_cpu
     if copy_ref and ("gdn", args.pools) in res:
         dec = rate(("gdn", args.pools), BYTES_GDN)
         detail["copy_reference"] = {
