@@ -20,7 +20,7 @@
 //
 // Cost model (gfx950): every byte of the unit is read once and written once
 // with 128-bit buffer accesses (non-temporal, except the FP16-row stores, see
-// below).  The VALU work is about 10.6 instructions per state value: convert,
+// below).  The VALU work is about 10.5 instructions per state value: convert,
 // scale, two reduction FMAs, the update FMA, half an absmax, a
 // four-instruction exact quantizer whose last step also packs the code byte,
 // and per-row / per-unit overheads.  Six workgroups fit per CU (168 VGPRs,
@@ -34,7 +34,6 @@
 #include "qrs_hadamard.h"
 
 namespace qrs {
-
 
 // KIND 0: GDN (gate = alpha [n][H]); KIND 1: KDA (gate = g [n][H][128]).
 // CODEC 0: the INT8 tier (symmetric codes, FP32 scale); CODEC 1: the first
@@ -57,9 +56,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((
     amdgpu_waves_per_eu(DecodeOccupancy<CODEC>::waves, DecodeOccupancy<CODEC>::waves))) void
 decode_packed_kernel(
     PoolView pool, const int32_t *__restrict__ slots, int first_gen, int n_cus, int h0, int hc,
-    const void *__restrict__ q,
-    const void *__restrict__ k, const void *__restrict__ v, const float *__restrict__ gate,
-    const float *__restrict__ beta, void *__restrict__ o) {
+    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
+    const float *__restrict__ gate, const float *__restrict__ beta, void *__restrict__ o) {
     __shared__ float s_k[DK];
     __shared__ float s_q[DK];
     __shared__ float s_dec[DK];
@@ -73,9 +71,9 @@ decode_packed_kernel(
     __shared__ float4 red_z[16][DV / 4];
 
     // Staggered start of the first generation (the workgroups resident at
-    // launch, first_gen = 0 when the grid is too small to benefit): the
-    // j-th workgroup placed on each CU waits j x ~0.85 us, so the first
-    // workgroups get their state sooner and compute while the others
+    // launch; first_gen = 0 when the grid is too small to benefit): the j-th
+    // workgroup placed on each CU waits j x 2048 cycles (~0.85 us), so the
+    // first workgroups get their state sooner and compute while the others
     // load, instead of all loading and then all computing at once.
     if ((int)blockIdx.x < first_gen) {
         const int j = (int)blockIdx.x / n_cus;
