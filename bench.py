@@ -499,6 +499,12 @@ def main():
                                       perm1, c1, n, H, steps, warmup, pools, use_graph)
                 res[("gdn", pools)] = (secs, ok)
                 log(f"[bench] gdn pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+            if use_graph:
+                # the same steps as launched one by one (no graph)
+                secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_I8F16, gdn_in,
+                                      perm1, c1, n, H, steps, warmup, args.pools, False)
+                res[("gdneager", args.pools)] = (secs, ok)
+                log(f"[bench] gdn eager launches pools={args.pools}: {secs / steps * 1e6:.2f} us/step")
             # the same bytes as one decode step, half read and half written
             copy_ref = run_copy_reference(torch, n * H * BYTES_GDN // 2)
             log(f"[bench] device copy of the same bytes: {copy_ref[0] * 1e6:.2f} us, {copy_ref[1]:.0f} GB/s")
@@ -624,7 +630,8 @@ def main():
     out = {}
     head_key = ("gdn", args.pools) if ("gdn", args.pools) in res else next(iter(res))
     kind0 = head_key[0]
-    NB = {"gdn": BYTES_GDN, "gdnv1": BYTES_GDN, "gdnbf16io": BYTES_GDN_BF16IO, "kda": BYTES_KDA,
+    NB = {"gdn": BYTES_GDN, "gdneager": BYTES_GDN, "gdnv1": BYTES_GDN, "gdnbf16io": BYTES_GDN_BF16IO,
+          "kda": BYTES_KDA,
           "f32": BYTES_F32_GDN}
     nbytes0 = NB[kind0]
     head = rate(head_key, nbytes0)
