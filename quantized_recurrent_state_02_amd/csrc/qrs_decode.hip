@@ -31,6 +31,8 @@
 // memory side alone did not move it: workgroups that prefetch a second unit,
 // one wave per column half over a layout with contiguous column halves, and
 // single 16-byte scale accesses all measured the same or slower.
+#include <atomic>
+
 #include "qrs_hadamard.h"
 
 namespace qrs {
@@ -312,25 +314,28 @@ decode_packed_kernel(
 // Launcher (host): one workgroup per (slot, head) unit of heads [h0, h0 + hc).
 // The number of workgroups resident at launch (occupancy x CUs) is queried
 // once per device and kernel.
+// The cache is per device; host threads launching concurrently may both
+// query it first, which is harmless (they store the same values).
 template <int K, int C, int I>
 static void decode_residency(int *per_cu, int *cus) {
-    static int s_per[16], s_cus[16];
+    static std::atomic<int> s_per[16], s_cus[16];
     int dev = 0;
     *per_cu = 0;
     *cus = 1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return;
-    if (s_per[dev] == 0) {
-        int p = 0, c = 0;
+    int p = s_per[dev].load(std::memory_order_acquire);
+    int c = s_cus[dev].load(std::memory_order_relaxed);
+    if (p == 0) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, decode_packed_kernel<K, C, I>, THREADS,
                                                          0) != hipSuccess ||
             hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            c <= 0)
+            c <= 0 || p <= 0)
             return;
-        s_cus[dev] = c;
-        s_per[dev] = p;
+        s_cus[dev].store(c, std::memory_order_relaxed);
+        s_per[dev].store(p, std::memory_order_release);
     }
-    *per_cu = s_per[dev];
-    *cus = s_cus[dev];
+    *per_cu = p;
+    *cus = c;
 }
 // The stagger pays off only when later generations follow the first.
 #define QRS_DECODE_CASE(K, C, I)                                                                  \
