@@ -81,6 +81,10 @@ decode_packed_kernel(
         const int j = (int)blockIdx.x / n_cus;
         for (int i = 0; i < j; ++i) __builtin_amdgcn_s_sleep(32);
     }
+    // Raised wave priority until the state loads are issued: a workgroup
+    // that starts while the SIMD's other waves run long VALU stretches gets
+    // its loads out first (0.3-0.5 us per step).
+    __builtin_amdgcn_s_setprio(3);
     const int tid = threadIdx.x;
     const int H = pool.num_heads;
     const int b = blockIdx.x / hc;
@@ -130,6 +134,7 @@ decode_packed_kernel(
         sc_old[r - 1] = buf_loadf(st, off_sc + 256 * (r - 1), SC_OFF);
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- gather through pi: thread t takes stored row t ----
     const float beta_u = beta[uu];
