@@ -83,7 +83,8 @@ decode_packed_kernel(
     }
     // Raised wave priority until the state loads are issued: a workgroup
     // that starts while the SIMD's other waves run long VALU stretches gets
-    // its loads out first (0.3-0.5 us per step).
+    // its loads out first (KDA 0.2 us per step faster, GDN within noise; the
+    // same change slowed the FP32-state and per-window kernels).
     __builtin_amdgcn_s_setprio(3);
     const int tid = threadIdx.x;
     const int H = pool.num_heads;
