@@ -46,12 +46,13 @@ __device__ __forceinline__ float lds_f32(const uint8_t *base, int byte_off) {
 }  // namespace
 
 template <int KIND>
-// Held to 168 VGPRs: three waves per SIMD (six units per CU) against two at
-// the 218 it took unconstrained, 6% faster per token in phase.  The last
-// replayed token forms its w and z partial sums in two passes and the store
-// offsets are re-derived after the replay, which leaves a few dwords of
-// spills (GDN: one value after the replay; KDA: one reload per replayed
-// token).
+// Held to 168 VGPRs: three waves per SIMD against two at the 218 it took
+// unconstrained, 6% faster per token in phase.  The last replayed token
+// forms its w and z partial sums in two passes and the store offsets are
+// re-derived after the replay, which leaves a few dwords of spills outside
+// the per-token work.  One 8 KB partial-sum buffer (not two) keeps the LDS of
+// a 16-token GDN window at 19 KB, so six workgroups fit per CU (five for KDA):
+// 4% faster per token in phase than with two buffers.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void window_kernel(
     PoolView pool, uint8_t *__restrict__ buf, int window, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ pos, const float *__restrict__ q, const float *__restrict__ k,
@@ -70,8 +71,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     __shared__ float s_coef[WIN_MAX];
     __shared__ float s_bd[DV];
     __shared__ float s_qk[2];
-    __shared__ float4 red_w[16][DV / 4];
-    __shared__ float4 red_z[16][DV / 4];
+    __shared__ float4 red[16][DV / 4];  // column partial sums (w or z)
     extern __shared__ __align__(16) uint8_t s_rec[];  // this window's earlier records, window * R bytes
 
     const int tid = threadIdx.x;
@@ -203,10 +203,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
                 }
                 pz[j] = az;
             }
-            red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
+            red[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
         }
         __syncthreads();
-        const float *rz = reinterpret_cast<const float *>(red_z);
+        const float *rz = reinterpret_cast<const float *>(red);
         float z = 0.f;
 #pragma unroll
         for (int g = 0; g < 16; ++g) z += rz[g * DV + tid];
@@ -305,8 +305,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 #pragma unroll
                 for (int c = 0; c < COLS_PER_THREAD; ++c) XV(r, c) = dr[r] * XV(r, c);
         }
-        // w partials, then (last token only) z partials in a second pass, so
-        // that kr and qr are not live together beside the state
+        // w partials; at the window's last token the z partials follow in the
+        // same buffer once every thread has read the w sums (one more barrier
+        // on that token only, one 8 KB buffer instead of two)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             float pw[4];
@@ -318,8 +319,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
                 for (int r = 1; r < ROWS_PER_THREAD; ++r) aw = __builtin_fmaf(kr[r], XV(r, c), aw);
                 pw[j] = aw;
             }
-            red_w[rg][cb * 4 + c4] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+            red[rg][cb * 4 + c4] = make_float4(pw[0], pw[1], pw[2], pw[3]);
         }
+        __syncthreads();
+        float bd;
+        {
+            const float *rw = reinterpret_cast<const float *>(red);
+            float w = 0.f;
+#pragma unroll
+            for (int g = 0; g < 16; ++g) w += rw[g * DV + tid];
+            bd = bt * (vp - w);
+            s_bd[tid] = bd;
+        }
+        __syncthreads();
         if (t == p) {
             float qr[ROWS_PER_THREAD];
 #pragma unroll
@@ -337,28 +349,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
                         az = __builtin_fmaf(qr[r], XV(r, c), az);
                     pz[j] = az;
                 }
-                red_z[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
+                red[rg][cb * 4 + c4] = make_float4(pz[0], pz[1], pz[2], pz[3]);
             }
-        }
-        __syncthreads();
-        {
-            const float *rw = reinterpret_cast<const float *>(red_w);
-            float w = 0.f;
+            __syncthreads();
+            const float *rz = reinterpret_cast<const float *>(red);
+            float zz = 0.f;
 #pragma unroll
-            for (int g = 0; g < 16; ++g) w += rw[g * DV + tid];
-            const float bd = bt * (vp - w);
-            if (t == p) {
-                const float *rz = reinterpret_cast<const float *>(red_z);
-                float zz = 0.f;
-#pragma unroll
-                for (int g = 0; g < 16; ++g) zz += rz[g * DV + tid];
-                const float qk = s_qk[0] + s_qk[1];
-                __builtin_nontemporal_store(c_t * __builtin_fmaf(qk, bd, zz),
-                                            o + (size_t)uu * DV + tid);
-            }
-            s_bd[tid] = bd;
+            for (int g = 0; g < 16; ++g) zz += rz[g * DV + tid];
+            const float qk = s_qk[0] + s_qk[1];
+            __builtin_nontemporal_store(c_t * __builtin_fmaf(qk, bd, zz), o + (size_t)uu * DV + tid);
         }
-        __syncthreads();
         float bdc[COLS_PER_THREAD];
 #pragma unroll
         for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb * 16 + c];
