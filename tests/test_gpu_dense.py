@@ -79,3 +79,31 @@ def test_dense_full_shape_sampled(kind, cfg):
     wl = inputs.WORKLOADS[cfg]
     sample = np.sort(np.random.default_rng(100 + cfg).choice(wl.n, 2, replace=False))
     print(run_dense(cfg, kind, wl.n, wl.heads, wl.steps, sample, True))
+
+
+@pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
+def test_dense_head_range_equals_full_call(kind, cfg):
+    """qrs_decode_step_ex on an FP32 pool with the head range [1, 4) of 6:
+    those heads equal a full-range call on a twin pool bit for bit (same
+    kernel arithmetic per unit), outputs of the other heads stay untouched
+    (NaN as prefilled) and their states do not change."""
+    n, H, steps, h0, hc = 5, 6, 4, 1, 3
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    S0 = to_dev(inputs.initial_state(cfg, n, H))
+    slots = to_dev(np.array([4, 0, 2, 1, 3], np.int32), torch.int32)
+    part = binding.StatePool(binding.FMT_FP32, n, H, perm, c)
+    full = binding.StatePool(binding.FMT_FP32, n, H, perm, c)
+    part.store(slots, S0)
+    full.store(slots, S0)
+    before = part.units().clone().view(n, H, -1)
+    for t in range(steps):
+        d = {key: to_dev(val) for key, val in inputs.step_inputs(cfg, t, n, H, kind).items()}
+        op = part.step_ex(kind, slots, d["q"], d["k"], d["v"], _gate(d, kind), d["beta"],
+                          heads=(h0, hc))
+        of = full.step_ex(kind, slots, d["q"], d["k"], d["v"], _gate(d, kind), d["beta"])
+        assert torch.equal(op[:, h0:h0 + hc].view(torch.int32), of[:, h0:h0 + hc].view(torch.int32))
+        assert torch.isnan(op[:, :h0]).all() and torch.isnan(op[:, h0 + hc:]).all()
+    up, uf = part.units().view(n, H, -1), full.units().view(n, H, -1)
+    assert torch.equal(up[:, h0:h0 + hc], uf[:, h0:h0 + hc])
+    assert torch.equal(up[:, :h0], before[:, :h0]) and torch.equal(up[:, h0 + hc:], before[:, h0 + hc:])
