@@ -499,6 +499,17 @@ def main():
                                       perm1, c1, n, H, steps, warmup, pools, use_graph)
                 res[("gdn", pools)] = (secs, ok)
                 log(f"[bench] gdn pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+            if args.only == "all":
+                # one GPU's share under 8-way tensor parallelism: 4 of the 32
+                # heads of every slot (1,024 units per step)
+                h4 = 4
+                in4 = {key: val[:, :, :h4].contiguous() for key, val in gdn_in.items()}
+                secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_I8F16, in4,
+                                      inputs.protected_perm(1, h4), inputs.smoothing(1, h4, True),
+                                      n, h4, steps, warmup, args.pools, use_graph)
+                res[("gdnh4", args.pools)] = (secs, ok)
+                log(f"[bench] gdn 256 x 4 heads (TP8 share): {secs / steps * 1e6:.2f} us/step")
+                del in4
             if use_graph:
                 # the same steps as launched one by one (no graph)
                 secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_I8F16, gdn_in,
@@ -587,7 +598,7 @@ def main():
     def rate(key, nbytes):
         secs, ok = res[key]
         per_step = secs / steps
-        ups = units / per_step
+        ups = (n * 4 if key[0] == "gdnh4" else units) / per_step
         return {"us_per_step": per_step * 1e6, "updates_per_s": ups,
                 "gbs": ups * nbytes / 1e9, "frac_of_peak": ups * nbytes / 1e9 / PEAK_HBM_GBS,
                 "finite_outputs": ok}
@@ -630,7 +641,8 @@ def main():
     out = {}
     head_key = ("gdn", args.pools) if ("gdn", args.pools) in res else next(iter(res))
     kind0 = head_key[0]
-    NB = {"gdn": BYTES_GDN, "gdneager": BYTES_GDN, "gdnv1": BYTES_GDN, "gdnbf16io": BYTES_GDN_BF16IO,
+    NB = {"gdn": BYTES_GDN, "gdneager": BYTES_GDN, "gdnh4": BYTES_GDN, "gdnv1": BYTES_GDN,
+          "gdnbf16io": BYTES_GDN_BF16IO,
           "kda": BYTES_KDA,
           "f32": BYTES_F32_GDN}
     nbytes0 = NB[kind0]
