@@ -255,17 +255,25 @@ BYTES_GDN_WINDOW = (20224 + 20224 / WINDOW + 528 * (WINDOW - 1) / 2 + 528 * (WIN
 
 
 def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph, reps=16,
-               staggered=False):
+               staggered=False, ends_first=False):
     """GDN per-window decode at the serving shape, `reps` whole windows timed;
     returns (seconds per token step, ok).  Every slot in the same phase, or
     (staggered) slot s at position (s + t) mod window at step t, so that each
-    step has slots at every position and 1/window of them end their window."""
+    step has slots at every position and 1/window of them end their window.
+    ends_first: the batch lists the slots by descending window position at
+    every step (a scheduling choice of the caller), so the requests that
+    replay their window come first in the grid."""
     pool = binding.StatePool(binding.FMT_I8F16, n, H, perm, c)
     slots = torch.arange(n, dtype=torch.int32, device="cuda")
     pool.store(slots, torch.from_numpy(inputs.initial_state(1, n, H)).to("cuda"))
     buf = pool.window_buffer("gdn", WINDOW)
+    order = [slots] * WINDOW
     if staggered:
         pos = [((torch.arange(n, device="cuda") + j) % WINDOW).to(torch.int32) for j in range(WINDOW)]
+        if ends_first:
+            order = [torch.sort(pj.long(), descending=True, stable=True).indices.to(torch.int32)
+                     for pj in pos]
+            pos = [pj[o.long()].contiguous() for pj, o in zip(pos, order)]
     else:
         pos = [torch.full((n,), j, dtype=torch.int32, device="cuda") for j in range(WINDOW)]
     out = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
@@ -273,7 +281,7 @@ def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph,
 
     def launch(t):
         tt = t % T
-        pool.window_step("gdn", WINDOW, buf, slots, pos[t % WINDOW], dev_in["q"][tt],
+        pool.window_step("gdn", WINDOW, buf, order[t % WINDOW], pos[t % WINDOW], dev_in["q"][tt],
                          dev_in["k"][tt], dev_in["v"][tt], dev_in["alpha"][tt], dev_in["beta"][tt],
                          out=out)
 
@@ -549,6 +557,16 @@ def main():
                 "frac_of_peak": n * H * BYTES_GDN_WINDOW / sec_s / 1e9 / PEAK_HBM_GBS,
                 "finite_outputs": ok_s}
             log(f"[bench] gdn per-window (16), staggered phases: {sec_s * 1e6:.2f} us/step ok={ok_s}")
+            sec_e, ok_e = run_window(torch, binding, inputs, gdn_in, perm1, c1, n, H, warmup,
+                                     use_graph, staggered=True, ends_first=True)
+            window_res["staggered_ends_first"] = {
+                "workload": "the same staggered phases, the batch ordered by descending window "
+                            "position at every step (window-end requests first in the grid)",
+                "us_per_step": sec_e * 1e6, "updates_per_s": n * H / sec_e,
+                "gbs": n * H * BYTES_GDN_WINDOW / sec_e / 1e9,
+                "frac_of_peak": n * H * BYTES_GDN_WINDOW / sec_e / 1e9 / PEAK_HBM_GBS,
+                "finite_outputs": ok_e}
+            log(f"[bench] gdn per-window (16), staggered, window ends first: {sec_e * 1e6:.2f} us/step")
         if args.only in ("v1", "all"):
             secs, ok = run_decode(torch, binding, inputs, "gdn", binding.FMT_U8H16, gdn_in, perm1,
                                   c1, n, H, steps, warmup, args.pools, use_graph)

@@ -224,6 +224,10 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
  *     position out of range leaves everything untouched and gives NaN
  *     outputs.
  * q, k, v, o: FP32 [n][H][128] as for the other decode calls.
+ * Scheduling: the window's last token replays the window's updates and takes
+ * several times longer than the others; workgroups follow the order of the
+ * batch, so listing the requests at position window - 1 first lets those
+ * start first (the results do not depend on the order).
  * QRS_EUNSUPPORTED on other pool formats.
  */
 size_t qrs_window_buffer_bytes(int kind, int num_slots, int num_heads, int window);
