@@ -385,6 +385,18 @@ def cpu_select_baseline(H, samples=192):
             "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))}
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_prefill_baseline(inputs, seqs=1, tokens=4096):
     """The oracle's chunked prefill (sequential FP32 recurrence inside each
     chunk of 64, compressed chunk ends) on a bounded sample of the prefill
@@ -461,13 +473,32 @@ def main():
                     default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--oracle-only", action="store_true",
+                    help="time the oracle alone (CPU; used for the single-thread figure)")
     args = ap.parse_args()
+
+    if args.oracle_only:
+        from quantized_recurrent_state_02_amd import inputs
+        print(json.dumps(cpu_baseline(inputs, "gdn", budget_s=4.0)))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not "
                                    "part of this build (decode units shard by slot or head "
                                    "with no exchange)", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    # The oracle on one thread, in a child process started before this one
+    # touches the GPU (OpenMP fixes its thread count when the library loads).
+    cpu_1t = None
+    if not args.no_cpu_baseline and args.only == "all":
+        import subprocess
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-only"],
+                           env=env, capture_output=True, text=True, timeout=300)
+        if r.returncode == 0 and r.stdout.strip():
+            cpu_1t = json.loads(r.stdout.strip().splitlines()[-1])
+            log(f"[bench] cpu oracle, 1 thread: {cpu_1t['value']:.3e} updates/s")
 
     import torch
     from quantized_recurrent_state_02_amd import binding, inputs
@@ -692,6 +723,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inputs, "gdn" if kind0 != "kda" else "kda")
+        cpu["cpu_model"] = cpu_model()
+        if cpu_1t is not None:
+            cpu["one_thread"] = {"value": cpu_1t["value"], "sample": cpu_1t["sample"]}
         log(f"[bench] cpu oracle: {cpu['value']:.3e} updates/s on {cpu['cores']} threads")
 
     traffic = traffic_from_profile(units) if kind0 == "gdn" else None
