@@ -2,8 +2,9 @@
 // disabled): the deployment default the compressed format is compared with
 // (DAMP arXiv HTML, section 6.1 "Inference": FP32 recurrent-state storage as
 // the baseline).  Same delta-rule update and readout as the fused kernel
-// (HTML section 3.1, Eq.(1)), same thread mapping and stored coordinates;
-// each unit is 65,536 bytes of FP32 read and written once.
+// (HTML section 3.1, Eq.(1)), the same rows per thread (its columns are
+// interleaved, below) and the same stored coordinates; each unit is 65,536
+// bytes of FP32 read and written once.
 #include "qrs_internal.h"
 
 namespace qrs {
