@@ -72,7 +72,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     __shared__ float s_bd[DV];
     __shared__ float s_qk[2];
     __shared__ float4 red[16][DV / 4];  // column partial sums (w or z)
-    extern __shared__ __align__(16) uint8_t s_rec[];  // this window's earlier records, window * R bytes
+    extern __shared__ __align__(16) uint8_t s_rec[];  // this window's earlier records, (window - 1) * R bytes
 
     const int tid = threadIdx.x;
     const int uu = blockIdx.x;
@@ -416,7 +416,8 @@ hipError_t launch_window(int kind, const PoolView &pool, uint8_t *buf, int windo
                          const float *k, const float *v, const float *gate, const float *beta,
                          float *o, hipStream_t stream) {
     dim3 grid((unsigned)(n * pool.num_heads)), block(THREADS);
-    const size_t lds = (size_t)window * window_record_bytes(kind);
+    // at most window - 1 earlier records are staged (the current token's is not)
+    const size_t lds = (size_t)(window - 1) * window_record_bytes(kind);
     if (kind == 0)
         hipLaunchKernelGGL(window_kernel<0>, grid, block, lds, stream, pool, buf, window, slots,
                            pos, q, k, v, gate, beta, o);
