@@ -42,6 +42,7 @@
 // row are exactly one 32-value group, held by the 16 lanes of a DPP row (two
 // values per lane), so a group's scale, or the block-32 transform and
 // extremes of the INT8+Hadamard tier, never leave the wave.
+#include <atomic>
 #include <cstddef>
 
 #include "qrs_hadamard.h"
@@ -612,6 +613,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
     }
 }
 
+// The kernel's dynamic LDS (about 152 KB) needs the function attribute raised,
+// once per device; host threads that get here together set it twice, which is
+// harmless.
 hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, int n, int T,
                           int chunk, int in_bf16, const void *q, const void *k, const void *v,
                           const float *alpha, const float *beta, float *o, int init_from_pool,
@@ -620,13 +624,16 @@ hipError_t launch_prefill(int fmt, const PoolView &pool, const int32_t *slots, i
     dim3 grid((unsigned)(n * pool.num_heads)), block(PT);
 #define QRS_PREFILL_CASE(F, B)                                                                    \
     if (fmt == F && in_bf16 == B) {                                                               \
-        static bool attr_set = false;                                                             \
-        if (!attr_set) {                                                                          \
+        static std::atomic<bool> attr_set[16];                                                    \
+        int dev = 0;                                                                              \
+        const hipError_t de = hipGetDevice(&dev);                                                 \
+        if (de != hipSuccess) return de;                                                          \
+        if (dev < 0 || dev >= 16 || !attr_set[dev].load(std::memory_order_acquire)) {             \
             hipError_t e = hipFuncSetAttribute(                                                   \
                 reinterpret_cast<const void *>(&prefill_kernel<F, B>),                            \
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);                           \
             if (e != hipSuccess) return e;                                                        \
-            attr_set = true;                                                                      \
+            if (dev >= 0 && dev < 16) attr_set[dev].store(true, std::memory_order_release);       \
         }                                                                                         \
         hipLaunchKernelGGL((prefill_kernel<F, B>), grid, block, smem, stream, pool, slots, T,     \
                            chunk, q, k, v, alpha, beta, o, init_from_pool);                       \
