@@ -30,7 +30,7 @@ def _sync_oracle(wo, gp, slots):
         wo.records[s] = []
 
 
-@pytest.mark.parametrize("window", [1, 5, 16, 24])
+@pytest.mark.parametrize("window", [1, 5, 16, 24, 32])
 @pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
 def test_windows_match_oracle(kind, cfg, window):
     n, H, num_slots = 6, 4, 9
