@@ -131,6 +131,13 @@ def test_invalid_position_and_slot():
                        to_dev(np.array([window, 0, -1], np.int32), torch.int32), q, q, q, g, g)
     assert torch.isnan(o).all()
     assert torch.equal(gp.units(), before) and torch.equal(buf, buf_before)
+    # an empty call enqueues nothing
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    ez = torch.empty((0, H, DK), device="cuda")
+    eg = torch.empty((0, H), device="cuda")
+    gp.window_step("gdn", window, buf, e32, e32, ez, ez, ez, eg, eg)
+    torch.cuda.synchronize()
+    assert torch.equal(gp.units(), before) and torch.equal(buf, buf_before)
     with pytest.raises(binding.QrsError, match="UNSUPPORTED"):
         binding.StatePool(binding.FMT_U8H16, 3, H).window_step(
             "gdn", window, buf, ds, to_dev(np.zeros(3, np.int32), torch.int32), q, q, q, g, g)
