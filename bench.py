@@ -252,10 +252,13 @@ def run_codec_compare(torch, binding, inputs, dev_in, perm, c, n, H, steps):
 WINDOW = 16
 BYTES_GDN_WINDOW = (20224 + 20224 / WINDOW + 528 * (WINDOW - 1) / 2 + 528 * (WINDOW - 1) / WINDOW
                     + 3 * 512 + 8)
+# KDA: records of 1,040 B (k, v FP16, g FP32 [128], beta), gates g and beta.
+BYTES_KDA_WINDOW = (20224 + 20224 / WINDOW + 1040 * (WINDOW - 1) / 2 + 1040 * (WINDOW - 1) / WINDOW
+                    + 3 * 512 + 512 + 4)
 
 
 def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph, reps=16,
-               staggered=False, ends_first=False):
+               staggered=False, ends_first=False, kind="gdn"):
     """GDN per-window decode at the serving shape, `reps` whole windows timed;
     returns (seconds per token step, ok).  Every slot in the same phase, or
     (staggered) slot s at position (s + t) mod window at step t, so that each
@@ -265,8 +268,9 @@ def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph,
     replay their window come first in the grid."""
     pool = binding.StatePool(binding.FMT_I8F16, n, H, perm, c)
     slots = torch.arange(n, dtype=torch.int32, device="cuda")
-    pool.store(slots, torch.from_numpy(inputs.initial_state(1, n, H)).to("cuda"))
-    buf = pool.window_buffer("gdn", WINDOW)
+    pool.store(slots, torch.from_numpy(inputs.initial_state(1 if kind == "gdn" else 2, n, H)).to("cuda"))
+    buf = pool.window_buffer(kind, WINDOW)
+    gate = "alpha" if kind == "gdn" else "g"
     order = [slots] * WINDOW
     if staggered:
         pos = [((torch.arange(n, device="cuda") + j) % WINDOW).to(torch.int32) for j in range(WINDOW)]
@@ -281,8 +285,8 @@ def run_window(torch, binding, inputs, dev_in, perm, c, n, H, warmup, use_graph,
 
     def launch(t):
         tt = t % T
-        pool.window_step("gdn", WINDOW, buf, order[t % WINDOW], pos[t % WINDOW], dev_in["q"][tt],
-                         dev_in["k"][tt], dev_in["v"][tt], dev_in["alpha"][tt], dev_in["beta"][tt],
+        pool.window_step(kind, WINDOW, buf, order[t % WINDOW], pos[t % WINDOW], dev_in["q"][tt],
+                         dev_in["k"][tt], dev_in["v"][tt], dev_in[gate][tt], dev_in["beta"][tt],
                          out=out)
 
     steps = reps * WINDOW
@@ -515,6 +519,7 @@ def main():
     units = n * H
     res = {}
     kda_cpu = None
+    kda_window = None
 
     if args.calib_copy_mb:
         nb = args.calib_copy_mb << 20
@@ -617,6 +622,17 @@ def main():
                                   c2, n, H, steps, warmup, pools, use_graph)
             res[("kda", pools)] = (secs, ok)
             log(f"[bench] kda pools={pools}: {secs / steps * 1e6:.2f} us/step ok={ok}")
+        if args.only == "all":
+            sec_k, ok_k = run_window(torch, binding, inputs, kda_in, perm2, c2, n, H, warmup,
+                                     use_graph, kind="kda")
+            kda_window = {
+                "workload": "KDA, 256 slots x 32 heads, windows of 16 tokens, all slots in phase",
+                "us_per_step": sec_k * 1e6, "updates_per_s": n * H / sec_k,
+                "bytes_per_update": BYTES_KDA_WINDOW,
+                "gbs": n * H * BYTES_KDA_WINDOW / sec_k / 1e9,
+                "frac_of_peak": n * H * BYTES_KDA_WINDOW / sec_k / 1e9 / PEAK_HBM_GBS,
+                "finite_outputs": ok_k}
+            log(f"[bench] kda per-window (16): {sec_k * 1e6:.2f} us/step ok={ok_k}")
         del kda_in
         if not args.no_cpu_baseline and args.only == "all":
             kda_cpu = cpu_baseline(inputs, "kda", budget_s=4.0)
@@ -712,6 +728,8 @@ def main():
         detail["window"] = window_res
     if kda_cpu:
         detail["kda_cpu_oracle"] = kda_cpu
+    if kda_window:
+        detail["kda_window"] = kda_window
     if copy_ref and ("gdn", args.pools) in res:
         dec = rate(("gdn", args.pools), BYTES_GDN)
         detail["copy_reference"] = {
