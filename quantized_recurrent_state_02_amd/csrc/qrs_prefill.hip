@@ -296,12 +296,20 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int t = lt + RPP * j;
+            float vv[VPL];
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 s.K[t * LDK + inv_c[i]] = elem(kr4[j], i);
                 s.Q[t * LDK + inv_c[i]] = elem(qr4[j], i);
-                s.VU[t * LDK + lc + i] = elem(vr4[j], i) / c_c[i];  // v' = D_c^{-1} v
+                vv[i] = elem(vr4[j], i) / c_c[i];  // v' = D_c^{-1} v
             }
+            // v' in model column order: whole 16-byte writes, each lane of a
+            // 16-lane group on its own banks (single floats four columns apart
+            // met four to a bank)
+#pragma unroll
+            for (int i = 0; i < VPL; i += 4)
+                *reinterpret_cast<v4f *>(&s.VU[t * LDK + lc + i]) =
+                    v4f{vv[i], vv[i + 1], vv[i + 2], vv[i + 3]};
         }
         // ---- 2. decay prefix sums (wave 0: lane = token) ----
         if (tid < CT) {
