@@ -17,9 +17,11 @@ sums, the GPU FP32 with FMAs and a tree of partial sums):
   The readout differs by at most c_j sum_i |q_i| dx_ij plus 2^-20 c_j 130
   sum_i |q_i| |T_ij|.
 * The bar of one quantization step per stored element after N steps is
-  checked on the final state: strictly on INT8 rows; on FP16 rows one FP16
-  ulp plus the coupling of the last step's INT8 differences through the
-  rank-1 write (see north_star_step_ok).
+  checked on the final state (north_star_step_ok): the two codes of an INT8
+  element differ by at most one step wherever the group scales agree to
+  rounding level and the last step's derived drift is below a step;
+  everywhere, one step plus that derived drift, which the per-step bounds
+  keep from growing with N.  FP16 rows: one FP16 ulp plus the same drift.
 """
 from __future__ import annotations
 
@@ -105,31 +107,83 @@ class StepBound:
         return prop + eps
 
 
-def north_star_step_ok(Tg, To, sg, so, coupling=None):
-    """One quantization step per stored element.
+def north_star_step_ok(Tg, To, sg, so, dx):
+    """The bar of one quantization step per stored element.
 
-    INT8 rows: the two codes differ by at most one step.  With scales s_g and
-    s_o (equal unless the group maxima differ by rounding) and |code| <= 127,
-    that is |T_gpu - T_orc| <= max(s_g, s_o) + 127 |s_g - s_o|, plus half an
-    FP32 ulp per side for the rounding of s * code.
-    FP16 rows: one FP16 ulp of the larger magnitude, plus ``coupling`` (the
-    pre-requantization difference bound of the last step, [..., 16, 128]):
-    INT8 codes of two correct implementations may differ by one step, and
-    every such difference reaches all rows through the rank-1 write
-    k' (beta delta)^T, so an FP16 row cannot be held to one ulp alone.
-    Returns (ok_lo, ok_hi, ok_hi_one_ulp, |difference|).
+    ``dx`` [..., 128, 128] is the derived bound on the difference of the two
+    sides' FP32 values just before the last requantization (StepBound.
+    pre_bound, or window_end_bound): the previous stored difference carried
+    through the decay and the rank-1 write, plus FP32 rounding.  The per-step
+    assertions keep the previous difference within one step, so dx contracts
+    with the decay and cannot grow with the number of steps.
+
+    INT8 rows.  Each side's stored value is within half its own step of its
+    FP32 value, so |T_gpu - T_orc| <= max(s_g, s_o) + dx everywhere (plus half
+    an FP32 ulp per side for the rounding of s * code): ``ok_lo``.  Where the
+    two group scales agree to rounding level (|s_g - s_o| <= 4 FP32 ulps of
+    the larger) and dx is below the smaller step, the two codes provably
+    differ by at most one, so the strict bar max(s) + 127 |s_g - s_o| applies:
+    ``ok_strict`` (True where it does not apply).  Scales further apart come
+    only from group maxima that differ by more than rounding, which dx
+    bounds.
+    FP16 rows: one FP16 ulp of the larger magnitude plus dx: ``ok_hi``; the
+    bare one-ulp count is ``ok_hi_ulp``.
+    Returns (ok_lo, ok_strict, ok_hi, ok_hi_ulp, stats) where stats reports
+    the fraction of INT8 elements beyond the bare one-step bar max(s), the
+    fraction of groups whose scales differ beyond rounding, the worst
+    |s_g - s_o| / max(s) and the worst excess over max(s) in units of max(s).
     """
     d = np.abs(Tg.astype(np.float64) - To.astype(np.float64))
+    dx = np.asarray(dx, dtype=np.float64)
     sg64, so64 = sg.astype(np.float64), so.astype(np.float64)
-    step = np.repeat(np.maximum(sg64, so64) + 127.0 * np.abs(sg64 - so64), 32, axis=-1)
+    smax = np.maximum(sg64, so64)
+    smin = np.minimum(sg64, so64)
+    ds = np.abs(sg64 - so64)
+    ulp32 = np.spacing(smax.astype(np.float32)).astype(np.float64)
+    rounding_level = ds <= 4.0 * ulp32
     # each dequantized value is s * code rounded to FP32: half an ulp per side
     rnd = 0.5 * (np.spacing(np.abs(Tg[..., 16:, :]).astype(np.float32)).astype(np.float64)
                  + np.spacing(np.abs(To[..., 16:, :]).astype(np.float32)).astype(np.float64))
-    ok_lo = d[..., 16:, :] <= step + rnd
+    step = np.repeat(smax, 32, axis=-1)
+    dlo = d[..., 16:, :]
+    ok_lo = dlo <= step + rnd + dx[..., 16:, :]
+    applies = np.repeat(rounding_level, 32, axis=-1) & \
+        (dx[..., 16:, :] <= (1 - 2.0 ** -12) * np.repeat(smin, 32, axis=-1))
+    strict = step + np.repeat(127.0 * ds * rounding_level, 32, axis=-1) + rnd
+    ok_strict = ~applies | (dlo <= strict)
     u16 = ulp16(np.maximum(np.abs(Tg[..., :16, :]), np.abs(To[..., :16, :])))
     ok_hi_ulp = d[..., :16, :] <= u16
-    ok_hi = ok_hi_ulp if coupling is None else d[..., :16, :] <= u16 + coupling
-    return ok_lo, ok_hi, ok_hi_ulp, d
+    ok_hi = d[..., :16, :] <= u16 + dx[..., :16, :]
+    beyond = dlo > step + rnd
+    stats = {"frac_int8_beyond_one_step": float(beyond.mean()) if beyond.size else 0.0,
+             "frac_groups_scale_beyond_rounding": float((~rounding_level).mean()) if ds.size else 0.0,
+             "worst_ds_over_s": float((ds / np.maximum(smax, 1e-300)).max()) if ds.size else 0.0,
+             "worst_excess_over_s": float(((dlo - step - rnd) / np.maximum(step, 1e-300)).max())
+             if dlo.size else 0.0,
+             "strict_bar_applies_frac": float(applies.mean()) if applies.size else 0.0,
+             "fp16_beyond_one_ulp": int((~ok_hi_ulp).sum())}
+    return ok_lo, ok_strict, ok_hi, ok_hi_ulp, stats
+
+
+def window_end_bound(bound, T0, tokens, b, h):
+    """Derived bound on |x_gpu - x_orc| before the requantization at a
+    window's last token, for unit (b, h): both sides start from the same
+    dequantized state T0 (stored space) and replay the window's tokens in
+    FP32 with k and v rounded to FP16, so the difference starts at zero and
+    grows only by each token's FP32 rounding, carried through the later
+    tokens (StepBound.pre_bound applied token by token; the magnitudes come
+    from an FP64 replay).  ``tokens`` lists the window's step-input dicts."""
+    D = np.zeros((DK, DV))
+    T = T0.astype(np.float64)
+    for d in tokens:
+        d16 = dict(d)
+        d16["k"] = d["k"].astype(np.float16).astype(np.float32)
+        d16["v"] = d["v"].astype(np.float16).astype(np.float32)
+        gate = d16["alpha"] if bound.kind == "gdn" else d16["g"]
+        k, q, lam, vp, beta = bound.operands(d16, b, h, gate)
+        D = bound.pre_bound(D, T, k, lam, vp, beta) * (1 + 2.0 ** -10)
+        T = lam[:, None] * T + np.outer(k, beta * (vp - (k * lam) @ T))
+    return D
 
 
 def describe_misses(ok_lo, Tg, To, sg, so, limit=4):

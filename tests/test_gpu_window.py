@@ -7,7 +7,10 @@ inside it the GPU computes outputs from the back-propagated query (one
 matrix-vector product over the stored state) and the oracle replays the
 buffered updates, so outputs agree to FP32 rounding; the stored bytes do not
 change until the window's last token, whose requantized state passes the
-one-quantization-step bar (codes within one step, FP16 rows within one ulp).
+one-quantization-step bar: both sides start the window from the same
+dequantized state, so their FP32 values before the requantization differ
+only by rounding (window_end_bound derives that difference token by token),
+and the codes differ by at most one step (FP16 rows one ulp) up to it.
 """
 import numpy as np
 import pytest
@@ -15,10 +18,27 @@ import torch
 
 import oracle
 from quantized_recurrent_state_02_amd import binding, inputs
-from tests.parity_util import north_star_step_ok, dequant_units, split_gpu, to_dev
+from tests.parity_util import (StepBound, dequant_units, describe_misses, north_star_step_ok,
+                               split_gpu, to_dev, window_end_bound)
 
 pytestmark = pytest.mark.gpu
 DK = DV = 128
+
+
+def _check_window_end(bound, gu, ou, T0, tokens_of, rows, H, what):
+    """The one-step bar on the window-end state of the units of `rows` (batch
+    rows of the step inputs), against the derived rounding drift."""
+    Tg, To = dequant_units(*gu), dequant_units(*ou)
+    dx = np.zeros(Tg.shape, dtype=np.float64)
+    for i, b in enumerate(rows):
+        for h in range(H):
+            dx[i * H + h] = window_end_bound(bound, T0[i * H + h], tokens_of(b), b, h)
+    ok_lo, ok_strict, ok_hi, _, st = north_star_step_ok(Tg, To, gu[2], ou[2], dx)
+    assert ok_lo.all() and ok_strict.all(), (
+        f"{what}: {(~ok_lo).sum()} INT8 elements beyond the bound, {(~ok_strict).sum()} beyond "
+        "the strict step: " + describe_misses(ok_lo & ok_strict, Tg, To, gu[2], ou[2]))
+    assert ok_hi.all(), f"{what}: FP16 rows beyond one ulp plus drift: {(~ok_hi).sum()}"
+    return st
 
 
 def _sync_oracle(wo, gp, slots):
@@ -45,12 +65,16 @@ def test_windows_match_oracle(kind, cfg, window):
     wo = oracle.OracleWindowPool(num_slots, H, perm, c, window)
     kid = 0 if kind == "gdn" else 1
     gate_key = "alpha" if kind == "gdn" else "g"
+    bound = StepBound(perm, c, kind)
     t = 0
     for w in range(windows):
         _sync_oracle(wo, gp, slots)
         start = gp.units().clone()
+        T0 = dequant_units(*split_gpu(gp, slots))
+        toks = []
         for j in range(window):
             d = inputs.step_inputs(cfg, t, n, H, kind)
+            toks.append(d)
             pos = np.full(n, j, np.int32)
             og = gp.window_step(kind, window, buf, ds, to_dev(pos, torch.int32), to_dev(d["q"]),
                                 to_dev(d["k"]), to_dev(d["v"]), to_dev(d[gate_key]),
@@ -65,13 +89,10 @@ def test_windows_match_oracle(kind, cfg, window):
                 assert torch.equal(gp.units(), start), f"window {w} token {j}: state written"
             t += 1
         gu = split_gpu(gp, slots)
-        H_ = H
-        idx = (slots[:, None] * H_ + np.arange(H_)[None, :]).ravel()
+        idx = (slots[:, None] * H + np.arange(H)[None, :]).ravel()
         ou = (wo.pool.hi[idx], wo.pool.lo[idx], wo.pool.sc[idx])
-        Tg, To = dequant_units(*gu), dequant_units(*ou)
-        ok_lo, ok_hi, _, d_ = north_star_step_ok(Tg, To, gu[2], ou[2])
-        assert ok_lo.all(), f"window {w}: INT8 rows beyond one step: {(~ok_lo).sum()}"
-        assert ok_hi.all(), f"window {w}: FP16 rows beyond one ulp: {(~ok_hi).sum()}"
+        st = _check_window_end(bound, gu, ou, T0, lambda b: toks, list(range(n)), H, f"window {w}")
+        print(f"window {w}: {st}")
 
 
 @pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
@@ -92,6 +113,8 @@ def test_mixed_positions_in_one_call(kind, cfg):
     wo = oracle.OracleWindowPool(num_slots, H, perm, c, window)
     kid = 0 if kind == "gdn" else 1
     gate_key = "alpha" if kind == "gdn" else "g"
+    bound = StepBound(perm, c, kind)
+    hist = {}     # batch row -> (dequantized window-start state, the window's inputs so far)
     ends = 0
     for t in range(steps):
         active = np.array([b for b in range(n) if b <= t], np.int64)
@@ -101,6 +124,10 @@ def test_mixed_positions_in_one_call(kind, cfg):
         if len(starting):
             _sync_oracle(wo, gp, starting)
         d = inputs.step_inputs(cfg, t, n, H, kind)
+        for b, p in zip(active.tolist(), pos.tolist()):
+            if p == 0:
+                hist[b] = (dequant_units(*split_gpu(gp, all_slots[[b]])), [])
+            hist[b][1].append(d)
         args = [np.ascontiguousarray(d[x][active]) for x in ("q", "k", "v", gate_key, "beta")]
         og = gp.window_step(kind, window, buf, to_dev(slots, torch.int32), to_dev(pos, torch.int32),
                             *(to_dev(a) for a in args)).cpu().numpy()
@@ -109,11 +136,13 @@ def test_mixed_positions_in_one_call(kind, cfg):
         assert err <= 1e-5, f"step {t}: readout error {err:.2e}"
         done = slots[pos == window - 1]
         if len(done):
+            rows = active[pos == window - 1].tolist()
             gu = split_gpu(gp, done)
             idx = (done[:, None] * H + np.arange(H)[None, :]).ravel()
             ou = (wo.pool.hi[idx], wo.pool.lo[idx], wo.pool.sc[idx])
-            ok_lo, ok_hi, _, _ = north_star_step_ok(dequant_units(*gu), dequant_units(*ou), gu[2], ou[2])
-            assert ok_lo.all() and ok_hi.all(), f"step {t}: window-end state of slots {done.tolist()}"
+            T0 = np.concatenate([hist[b][0] for b in rows])
+            _check_window_end(bound, gu, ou, T0, lambda b: hist[b][1], rows, H,
+                              f"step {t}: window-end state of slots {done.tolist()}")
             ends += len(done)
     assert ends >= 2 * n - 2
 
