@@ -67,6 +67,8 @@ def load():
     lib.orc_u8_prefill.argtypes = [p, p, p, i, p, p, p, i, i, i, p, p, p, p, p, p, i]
     lib.orc_unit_bytes.argtypes = []
     lib.orc_unit_bytes.restype = i64
+    lib.orc_max_threads.argtypes = []
+    lib.orc_max_threads.restype = i
     _lib = lib
     return lib
 
@@ -139,6 +141,11 @@ def quantize_group_u8(y: np.ndarray):
     sz = np.zeros(2, dtype=np.uint16)
     load().orc_quantize_group_u8(_ptr(y), _ptr(code), _ptr(sz[0:1]), _ptr(sz[1:2]))
     return code, sz[0], sz[1]
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's loops over units use."""
+    return int(load().orc_max_threads())
 
 
 def unit_bytes() -> int:

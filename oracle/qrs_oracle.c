@@ -47,6 +47,7 @@
  * OpenMP only splits independent (slot, head) units across threads.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -701,4 +702,10 @@ void orc_channel_error(const float *S, int n, int num_heads, const float *c, dou
 int64_t orc_unit_bytes(void)
 {
     return (int64_t)KHI * DV * 2 + (int64_t)KLO * DV * 1 + (int64_t)KLO * NGRP * 4;
+}
+
+/* Threads the OpenMP loops above use (reported beside the oracle's timings). */
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
 }
