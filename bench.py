@@ -92,7 +92,7 @@ def stage_inputs(torch, inputs, cfg, kind, n, H, steps):
     return dev
 
 
-def time_loop(torch, launch, steps, warmup, use_graph, reps=5, warm_s=0.0):
+def time_loop(torch, launch, steps, warmup, use_graph, reps=5, warm_s=0.0, side=None):
     """Run `launch(t)` for t < warmup (eager), then time `reps` passes over the
     steps t in [warmup, warmup + steps), back to back.
 
@@ -103,24 +103,33 @@ def time_loop(torch, launch, steps, warmup, use_graph, reps=5, warm_s=0.0):
     events on the launch stream that are recorded behind work already in the
     queue, so neither the host's graph submission nor an idle GPU falls
     inside a timed window.
+    `side`: a second stream that `launch` also issues work on; it is forked
+    from the launch stream before a pass's first step and joined after its
+    last (one fork and one join per pass, none per step).
     Returns (seconds of each timed pass, seconds of device warm-up)."""
     stream = torch.cuda.current_stream()
-    for t in range(warmup):
-        launch(t)
+
+    def steps_of(ts):
+        if side is not None:
+            side.wait_stream(torch.cuda.current_stream())
+        for t in ts:
+            launch(t)
+        if side is not None:
+            torch.cuda.current_stream().wait_stream(side)
+
+    steps_of(range(warmup))
     torch.cuda.synchronize()
     if use_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for t in range(warmup, warmup + steps):
-                launch(t)
+            steps_of(range(warmup, warmup + steps))
         torch.cuda.synchronize()
         g.replay()                       # graph upload
         torch.cuda.synchronize()
         run = g.replay
     else:
         def run():
-            for t in range(warmup, warmup + steps):
-                launch(t)
+            steps_of(range(warmup, warmup + steps))
     warm = 0.0
     if warm_s > 0:
         t0 = time.perf_counter()
@@ -485,10 +494,13 @@ PAGED_BYTES_PER_STEP = (PAGED_ACTIVE // 2) * 32 * (BYTES_GDN + BYTES_KDA)
 PAGED_UPDATES_PER_STEP = PAGED_ACTIVE * 32
 
 
-def run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=5, warm_s=0.5):
+def run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=5, warm_s=0.5, streams=1):
     """Paged decode, inputs drawn on the device with the workload's recipe
     (heavy-tailed initial states with outlier rows in the FP16 channels,
-    smoothing on).  Returns the pass_stats dict (seconds per step)."""
+    smoothing on).  streams=1: both calls of a step on one stream, in order;
+    streams=2: the KDA calls on a second stream (the two request groups share
+    no slot, so each group's steps stay in order on its own stream and the
+    two chains overlap).  Returns the pass_stats dict (seconds per step)."""
     cfg, H = 4, 32
     perm = inputs.protected_perm(cfg, H)
     c = inputs.smoothing(cfg, H, True)
@@ -508,12 +520,19 @@ def run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=5, warm_s=0
     dsl = {"gdn": torch.from_numpy(gdn_slots).to("cuda"), "kda": torch.from_numpy(kda_slots).to("cuda")}
     out = {kind: torch.empty((PAGED_ACTIVE // 2, H, 128), device="cuda") for kind in ("gdn", "kda")}
 
+    side = torch.cuda.Stream() if streams == 2 else None
+
     def launch(t):
         a, b = ins["gdn"][t], ins["kda"][t]
         pool.gdn_step(dsl["gdn"], a["q"], a["k"], a["v"], a["alpha"], a["beta"], out["gdn"])
-        pool.kda_step(dsl["kda"], b["q"], b["k"], b["v"], b["g"], b["beta"], out["kda"])
+        if side is None:
+            pool.kda_step(dsl["kda"], b["q"], b["k"], b["v"], b["g"], b["beta"], out["kda"])
+        else:
+            with torch.cuda.stream(side):
+                pool.kda_step(dsl["kda"], b["q"], b["k"], b["v"], b["g"], b["beta"], out["kda"])
 
-    passes, _ = time_loop(torch, launch, steps, warmup, use_graph, reps=reps, warm_s=warm_s)
+    passes, _ = time_loop(torch, launch, steps, warmup, use_graph, reps=reps, warm_s=warm_s,
+                          side=side)
     st = pass_stats(passes, steps)
     st["ok"] = all(bool(torch.isfinite(o).all().item()) for o in out.values())
     pool.close()
@@ -889,6 +908,19 @@ def main():
                  "us_per_step_at_70pct_of_peak": PAGED_BYTES_PER_STEP / (0.7 * PEAK_HBM_GBS * 1e9) * 1e6,
                  "finite_outputs": st["ok"]}
         log(f"[bench] paged mixed pool: {per * 1e6:.2f} us/step, {paged['frac_of_peak'] * 100:.1f}% of peak")
+        st2 = run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=reps, warm_s=leg_warm,
+                        streams=2)
+        per2 = st2["per_step"]
+        paged["two_streams"] = {
+            "workload": "the same steps, the KDA request group's calls on a second stream (one "
+                        "fork and one join per timed pass; each group's steps stay in order)",
+            "us_per_step": per2 * 1e6, "us_min": st2["per_step_min"] * 1e6,
+            "us_max": st2["per_step_max"] * 1e6, "updates_per_s": PAGED_UPDATES_PER_STEP / per2,
+            "gbs": PAGED_BYTES_PER_STEP / per2 / 1e9,
+            "frac_of_peak": PAGED_BYTES_PER_STEP / per2 / 1e9 / PEAK_HBM_GBS,
+            "finite_outputs": st2["ok"]}
+        log(f"[bench] paged mixed pool, two streams: {per2 * 1e6:.2f} us/step, "
+            f"{paged['two_streams']['frac_of_peak'] * 100:.1f}% of peak")
 
     sweep = None
     if args.only in ("sweep", "all"):

@@ -250,15 +250,19 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
     constexpr int LPR = DK / VPL;        // pieces per token row
     constexpr int RPP = PT / LPR;        // token rows per pass of the workgroup
     constexpr int NLD = CT / RPP;        // pieces per thread per input
-    const int lc = (tid % LPR) * VPL;
-    const int lt = tid / LPR;
-    int inv_c[VPL];
-    float c_c[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        inv_c[i] = s.inv[lc + i];
-        c_c[i] = pool.smooth[h * DV + lc + i];
-    }
+    // lc, lt and the per-thread pi / c entries are re-derived where they are
+    // used from an opaque copy of the thread id: held across the chunk loop
+    // they were spilled and reloaded every chunk (first revision's tier).
+    auto piece_col = [&]() {
+        int t2 = tid;
+        asm volatile("" : "+v"(t2));
+        return (t2 % LPR) * VPL;
+    };
+    auto piece_row = [&]() {
+        int t2 = tid;
+        asm volatile("" : "+v"(t2));
+        return t2 / LPR;
+    };
     U4 kr4[NLD], qr4[NLD], vr4[NLD];
     float a_in = 1.f, b_in = 0.f;
     // Part 0: k and the gates; part 1: q; part 2: v.  The parts are issued
@@ -272,6 +276,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         const void *src = part == 0 ? k : part == 1 ? q : v;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((const uint8_t *)src + row0 * DK * ESZ, bytes);
         U4 *dst = part == 0 ? kr4 : part == 1 ? qr4 : vr4;
+        const int lc = piece_col(), lt = piece_row();
 #pragma unroll
         for (int j = 0; j < NLD; ++j) dst[j] = buf_load16(rs, (lt + RPP * j) * rstride + lc * ESZ, 0);
         if (part == 0 && tid < CT) {
@@ -293,6 +298,14 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         const int t0 = ch * chunk;
         const int ceff = min(chunk, T - t0);
         // ---- 1. chunk operands into LDS (loaded during the previous chunk) ----
+        const int lc = piece_col(), lt = piece_row();
+        int inv_c[VPL];
+        float c_c[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            inv_c[i] = s.inv[lc + i];
+            c_c[i] = pool.smooth[h * DV + lc + i];
+        }
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
             const int t = lt + RPP * j;

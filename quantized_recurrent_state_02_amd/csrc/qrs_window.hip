@@ -22,7 +22,11 @@
 // Record of token t of slot s, head h, at buffer + ((s H + h) window + t) R:
 //   [0, 256) k FP16 [128], [256, 512) v FP16 [128] (model order);
 //   GDN (R = 528): [512] beta, [516] alpha (FP32);
-//   KDA (R = 1040): [512, 1024) g FP32 [128], [1024] beta.
+//   KDA (R = 1040): [512, 1024) exp(g) FP32 [128], [1024] beta.
+// The KDA record holds the decay factors exp(g) rather than g: exp runs once,
+// when the token is recorded, instead of at every later use (the query's
+// back-propagation through the window and the window-end replay), and the
+// values used are the same.
 #include "qrs_internal.h"
 
 namespace qrs {
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     const float beta_c = beta[uu];
     const float alpha_c = KIND == 0 ? gate[uu] : 0.f;
     const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
+    const float lam_c = KIND == 1 ? expf(g_c) : 0.f;   // this token's decay of key channel tid
     U4 hi_raw[2];
     U4 lo_raw[ROWS_PER_THREAD - 1];
     float sc_old[ROWS_PER_THREAD - 1];
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     if (!boundary) {
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k16, rb, p * R + 2 * tid, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v16, rb, p * R + 256 + 2 * tid, 0, 0);
-        if (KIND == 1) buf_storef(rb, g_c, p * R + 512 + 4 * tid, 0);
+        if (KIND == 1) buf_storef(rb, lam_c, p * R + 512 + 4 * tid, 0);
         if (tid == 0) {
             buf_storef(rb, beta_c, p * R + BOFF, 0);
             if (KIND == 0) buf_storef(rb, alpha_c, p * R + 516, 0);
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     s_kc[tid] = f16_bits_to_f32(k16);
     s_q[tid] = q_in;
     s_perm[tid] = perm_t;
-    if (KIND == 1) s_lam[tid] = expf(g_c);
+    if (KIND == 1) s_lam[tid] = lam_c;
     __syncthreads();
 
     if (!boundary) {
@@ -173,8 +178,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
                 ka = nka;
                 kb = nkb;
                 bt = nbt;
-                la = KIND == 0 ? nla : expf(nla);
-                lb = KIND == 0 ? nlb : expf(nlb);
+                la = nla;
+                lb = nlb;
             }
             s_x0[i0] = x0;
             s_x0[i1] = x1;
@@ -251,15 +256,23 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
         const float pqk = wave_allsum(s_q[tid] * f16_bits_to_f32(k16));
         if ((tid & 63) == 0) s_qk[tid >> 6] = pqk;
     }
-    const int ma[2] = {s_perm[rg + 16 * (cb & 3)], s_perm[rg + 16 * (4 + (cb & 3))]};
     // GDN: every row decays by the same alpha, so the state is kept as gam X
     // with gam the product of the window's alphas so far: a token's decay is
     // one multiply instead of one per value; w = sum (k gam) X and the write
     // adds (k / gam) (beta delta).  When gam falls below 2^-60 (a zero alpha
-    // included) it is folded back into X.  KDA decays its rows in place.
+    // included), and at the window's last token, it is folded back into X, so
+    // the state leaves the loop unscaled (a separate pass over it after the
+    // loop made the compiler spill).  KDA decays its rows in place.
     float gam = 1.f;
     for (int t = 0; t <= p; ++t) {
         float kr[ROWS_PER_THREAD], dr[ROWS_PER_THREAD], ka[2], bt, vp;
+        // The model channels of this lane's two rank-1 write operands, read
+        // each token from an opaque copy of the thread id: held across the
+        // replay they were spilled and reloaded with a full memory wait.
+        int tid2 = tid;
+        asm volatile("" : "+v"(tid2));
+        const int ma[2] = {s_perm[(tid2 >> 3) + 16 * (tid2 & 3)],
+                           s_perm[(tid2 >> 3) + 16 * (4 + (tid2 & 3))]};
         if (t < p) {
             const uint8_t *rec = s_rec + t * R;
             vp = lds_f16(rec, 256 + 2 * tid) / c_t;
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
             for (int r = 0; r < ROWS_PER_THREAD; ++r) {
                 const int m = s_perm[rg + 16 * r];
                 kr[r] = lds_f16(rec, 2 * m);
-                dr[r] = KIND == 0 ? at : expf(lds_f32(rec, 512 + 4 * m));
+                dr[r] = KIND == 0 ? at : lds_f32(rec, 512 + 4 * m);
             }
             ka[0] = lds_f16(rec, 2 * ma[0]);
             ka[1] = lds_f16(rec, 2 * ma[1]);
@@ -287,7 +300,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
         }
         if (KIND == 0) {
             gam *= dr[0];
-            if (gam < 0x1p-60f) {  // the same for every thread
+            if (gam < 0x1p-60f || t == p) {  // the same for every thread
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -368,13 +381,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
             for (int c = 0; c < COLS_PER_THREAD; ++c)
                 X[hh][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(ka[hh], bdc[c], X[hh][c], 0, 0, 0);
     }
-    if (KIND == 0) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int c = 0; c < COLS_PER_THREAD; ++c) X[hh][c] *= gam;
-    }
-
     // ---- requantize the window-end state into the pool (offsets re-derived
     //      from an opaque copy of the thread id rather than held across the
     //      replay) ----
@@ -394,17 +400,21 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     }
 #pragma unroll
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+        float xr[COLS_PER_THREAD];
         float amax = 0.f;
 #pragma unroll
-        for (int c = 0; c < COLS_PER_THREAD; ++c) amax = fmaxf(amax, fabsf(XV(r, c)));
+        for (int c = 0; c < COLS_PER_THREAD; ++c) {
+            xr[c] = XV(r, c);
+            amax = fmaxf(amax, fabsf(xr[c]));
+        }
         amax = pair_max(amax);
         const float s = group_scale(amax);
         const double rinv = pack_reciprocal(s);
         U4 cw;
-        cw.x = quant4(XV(r, 0), XV(r, 1), XV(r, 2), XV(r, 3), rinv);
-        cw.y = quant4(XV(r, 4), XV(r, 5), XV(r, 6), XV(r, 7), rinv);
-        cw.z = quant4(XV(r, 8), XV(r, 9), XV(r, 10), XV(r, 11), rinv);
-        cw.w = quant4(XV(r, 12), XV(r, 13), XV(r, 14), XV(r, 15), rinv);
+        cw.x = quant4(xr[0], xr[1], xr[2], xr[3], rinv);
+        cw.y = quant4(xr[4], xr[5], xr[6], xr[7], rinv);
+        cw.z = quant4(xr[8], xr[9], xr[10], xr[11], rinv);
+        cw.w = quant4(xr[12], xr[13], xr[14], xr[15], rinv);
         buf_store16(st, cw, off_lo2, LO_OFF + 2048 * (r - 1));
         if ((cb2 & 1) == 0) buf_storef(st, s, off_sc2 + 256 * (r - 1), SC_OFF);
     }
