@@ -735,6 +735,9 @@ def main():
                     default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--decode-split", choices=["auto", "whole", "halves"], default="auto",
+                    help="INT8-tier decode kernel: by grid size (default), one workgroup per "
+                         "unit, or two per unit (value-column halves)")
     ap.add_argument("--oracle-only", action="store_true",
                     help="time the oracle alone (CPU; used for the single-thread figure)")
     args = ap.parse_args()
@@ -769,6 +772,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     binding.load()
+    binding.set_decode_split({"auto": binding.DECODE_SPLIT_AUTO, "whole": binding.DECODE_SPLIT_WHOLE,
+                              "halves": binding.DECODE_SPLIT_HALVES}[args.decode_split])
     torch.cuda.set_device(0)
     n, H = 256, 32
     steps, warmup, reps = args.steps, args.warmup, args.reps
@@ -993,6 +998,7 @@ def main():
               "frac": paged["frac_of_peak"], "traffic": None}, {"paged": paged})
         return
     if not res and sweep:    # --only sweep
+        sweep["decode_split"] = args.decode_split
         b256 = sweep["batches"]["256"]
         diag("decode speedup of the compressed state over the FP32 state, batch sweep",
              b256["gdn_speedup_vs_fp32_state"], "x", sweep["workload"],
@@ -1016,7 +1022,7 @@ def main():
           "f32": BYTES_F32_GDN}
     nbytes0 = NB[kind0]
     head = rate(head_key, nbytes0)
-    detail = {"device_warmup_s": res[head_key]["device_warmup_s"],
+    detail = {"device_warmup_s": res[head_key]["device_warmup_s"], "decode_split": args.decode_split,
               "timing": f"median of {reps} timed passes of {steps} steps each, every pass "
                         "bracketed by HIP events recorded behind an already-enqueued untimed "
                         "pass; min and max beside each figure"}

@@ -333,6 +333,31 @@ int qrs_channel_scores(int n, int num_heads, const double *e, const double *W, c
 int qrs_select_protected_channels(int num_heads, const double *score_host, int k_hi,
                                   int32_t *perm_host);
 
+/*
+ * Which kernel the QRS_FMT_I8F16 decode steps (qrs_gdn_decode_step,
+ * qrs_kda_decode_step, qrs_decode_step_ex) launch.  Every step of the update
+ * stays within a value column (DAMP HTML, section 3.1 Eq.(1); the v2 notes'
+ * 32-value groups run along the value axis), so a unit can be split into two
+ * workgroups, one per 64-column half, with no exchange between them.  Both
+ * kernels perform the same operations in the same order and give the same
+ * bits; they differ only in speed:
+ *   QRS_DECODE_SPLIT_WHOLE:  one workgroup per (slot, head) unit;
+ *   QRS_DECODE_SPLIT_HALVES: two workgroups per unit, for grids too small to
+ *     fill the GPU (a whole-unit workgroup's lifetime then sets the step);
+ *   QRS_DECODE_SPLIT_AUTO (the default): the halves below 1,024 units per call
+ *     (n * head count); on MI355X they are faster only there.
+ * The setting is process-wide, applies to calls enqueued after it returns,
+ * and is a tuning choice only.  Returns the previous mode (>= 0), or
+ * QRS_EINVAL for another value (the setting is then unchanged).  Other pool formats and the
+ * per-window step ignore it.
+ */
+enum {
+    QRS_DECODE_SPLIT_AUTO = 0,
+    QRS_DECODE_SPLIT_WHOLE = 1,
+    QRS_DECODE_SPLIT_HALVES = 2
+};
+int qrs_set_decode_split(int mode);
+
 /* Name of a status code (static string). */
 const char *qrs_status_string(int status);
 

@@ -23,6 +23,7 @@ FMT_U8H16 = 2
 SPACE_MODEL = 0
 SPACE_STORED = 1
 OK = 0
+DECODE_SPLIT_AUTO, DECODE_SPLIT_WHOLE, DECODE_SPLIT_HALVES = 0, 1, 2
 DK = DV = 128
 KHI = 16
 GRP = 32
@@ -35,7 +36,7 @@ EXPORTED = (
     "qrs_decode_step_ex", "qrs_window_buffer_bytes", "qrs_window_decode_step",
     "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
     "qrs_persistence_geometric", "qrs_channel_scores", "qrs_select_protected_channels",
-    "qrs_status_string",
+    "qrs_set_decode_split", "qrs_status_string",
 )
 
 _lib = None
@@ -71,6 +72,8 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [p, p, i, p, p, p, p, p, p, p]
         fn.restype = i
+    lib.qrs_set_decode_split.argtypes = [i]
+    lib.qrs_set_decode_split.restype = i
     lib.qrs_decode_step_ex.argtypes = [p, i, i, p, i, i, i, p, p, p, p, p, p, p]
     lib.qrs_decode_step_ex.restype = i
     lib.qrs_window_buffer_bytes.argtypes = [i, i, i, i]
@@ -115,6 +118,16 @@ def _dev(t: torch.Tensor, dtype, shape, name):
     if not t.is_contiguous():
         raise QrsError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def set_decode_split(mode: int) -> int:
+    """Choose the INT8-tier decode kernel (qrs_set_decode_split): one
+    workgroup per unit, two per unit (value-column halves), or by grid size
+    (the default).  Returns the previous mode."""
+    prev = load().qrs_set_decode_split(int(mode))
+    if prev < 0:
+        raise QrsError(f"qrs_set_decode_split({mode}): invalid mode")
+    return prev
 
 
 def pool_bytes(fmt: int, num_slots: int, num_heads: int) -> int:

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <new>
 #include <algorithm>
+#include <atomic>
 #include <numeric>
 #include <vector>
 
@@ -13,6 +14,9 @@
 #include "qrs_internal.h"
 
 namespace qrs {
+hipError_t launch_decode_half(int kind, int io, const PoolView &pool, const int32_t *slots, int n,
+                              int h0, int hc, const void *q, const void *k, const void *v,
+                              const float *gate, const float *beta, void *o, hipStream_t stream);
 hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &pool,
                                 const int32_t *slots, int n, int h0, int hc, const void *q,
                                 const void *k, const void *v, const float *gate, const float *beta,
@@ -113,6 +117,18 @@ struct DeviceGuard {
     }
 };
 
+// Which INT8-tier decode kernel runs: one workgroup per unit, or two per unit
+// (value-column halves) for grids too small to fill the GPU.
+// QRS_DECODE_SPLIT_AUTO picks the halves below kDecodeSplitUnits units.
+std::atomic<int> g_decode_split{QRS_DECODE_SPLIT_AUTO};
+constexpr int kDecodeSplitUnits = 1024;
+
+bool use_half_kernel(int units) {
+    const int mode = g_decode_split.load(std::memory_order_relaxed);
+    if (mode == QRS_DECODE_SPLIT_AUTO) return units < kDecodeSplitUnits;
+    return mode == QRS_DECODE_SPLIT_HALVES;
+}
+
 int decode_common(int kind, int io, qrs_pool pool, const int32_t *slots, int n, int h0, int hc,
                   const void *q, const void *k, const void *v, const float *gate,
                   const float *beta, void *o, hipStream_t stream) {
@@ -130,6 +146,8 @@ int decode_common(int kind, int io, qrs_pool pool, const int32_t *slots, int n, 
             ? qrs::launch_decode_f32(kind, pv, slots, n, h0, hc, static_cast<const float *>(q),
                                      static_cast<const float *>(k), static_cast<const float *>(v),
                                      gate, beta, static_cast<float *>(o), stream)
+        : pool->fmt == QRS_FMT_I8F16 && use_half_kernel(n * hc)
+            ? qrs::launch_decode_half(kind, io, pv, slots, n, h0, hc, q, k, v, gate, beta, o, stream)
             : qrs::launch_decode_packed(kind, pool->fmt == QRS_FMT_U8H16 ? 1 : 0, io, pv, slots, n,
                                         h0, hc, q, k, v, gate, beta, o, stream);
     return e == hipSuccess ? QRS_OK : QRS_EDEVICE;
@@ -385,6 +403,13 @@ int qrs_select_protected_channels(int num_heads, const double *score_host, int k
             if (!chosen[u]) pm[pos++] = u;
     }
     return QRS_OK;
+}
+
+int qrs_set_decode_split(int mode) {
+    if (mode != QRS_DECODE_SPLIT_AUTO && mode != QRS_DECODE_SPLIT_WHOLE &&
+        mode != QRS_DECODE_SPLIT_HALVES)
+        return QRS_EINVAL;
+    return g_decode_split.exchange(mode, std::memory_order_relaxed);
 }
 
 const char *qrs_status_string(int status) {

@@ -173,3 +173,19 @@ def test_window_buffer_bytes_and_null_pool(lib):
     p = ctypes.c_void_p(0x10000)
     assert lib.qrs_window_decode_step(None, 0, 16, p, 1 << 20, p, p, 1, p, p, p, p, p, p,
                                       None) == -1
+
+
+def test_decode_split_setting(lib):
+    """qrs_set_decode_split: the three documented modes are accepted and
+    return the previous one; anything else is rejected and changes nothing."""
+    prev = lib.qrs_set_decode_split(binding.DECODE_SPLIT_WHOLE)
+    try:
+        assert prev in (0, 1, 2)
+        assert lib.qrs_set_decode_split(binding.DECODE_SPLIT_HALVES) == binding.DECODE_SPLIT_WHOLE
+        assert lib.qrs_set_decode_split(3) == -1                         # QRS_EINVAL
+        assert lib.qrs_set_decode_split(-1) == -1
+        assert lib.qrs_set_decode_split(binding.DECODE_SPLIT_AUTO) == binding.DECODE_SPLIT_HALVES
+        with pytest.raises(binding.QrsError):
+            binding.set_decode_split(5)
+    finally:
+        lib.qrs_set_decode_split(prev)

@@ -43,8 +43,18 @@ def _exact_inputs(r, n, H, kind):
     return d
 
 
+@pytest.fixture(params=["whole", "halves"])
+def split(request):
+    """Run a test with the whole-unit decode kernel and with the value-column
+    halves (both are bit-exact against the oracle on exact trajectories)."""
+    mode = binding.DECODE_SPLIT_WHOLE if request.param == "whole" else binding.DECODE_SPLIT_HALVES
+    prev = binding.set_decode_split(mode)
+    yield request.param
+    binding.set_decode_split(prev)
+
+
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-def test_exact_trajectory_bit_exact(kind):
+def test_exact_trajectory_bit_exact(kind, split):
     n, H, num_slots, steps = 3, 5, 7, 64
     r = np.random.default_rng(70 if kind == "gdn" else 71)
     perm = inputs.protected_perm(70, H)
@@ -158,7 +168,7 @@ def test_cfg0_gdn_small():
 
 
 @pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
-def test_reduced_serving_shape(kind, cfg):
+def test_reduced_serving_shape(kind, cfg, split):
     """32 heads, 12 slots on the GPU (384 workgroups), 3 of them followed by
     the oracle, 64 steps."""
     stats = run_parity(cfg, kind, 12, 32, 64, [0, 5, 11], smooth=True)
