@@ -127,6 +127,48 @@ __device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, float 
     }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Eight LDS values that are exact bf16 numbers (bf16 inputs widened to FP32:
+// the low 16 bits are zero) as the bf16 operand of one MFMA: the high half of
+// each, two per v_perm.
+__device__ __forceinline__ bf16x8 to_bf16x8(v4f lo, v4f hi) {
+    typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+    const auto b = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+    const u32x4_ w = {__builtin_amdgcn_perm(b(lo.y), b(lo.x), 0x07060302u),
+                      __builtin_amdgcn_perm(b(lo.w), b(lo.z), 0x07060302u),
+                      __builtin_amdgcn_perm(b(hi.y), b(hi.x), 0x07060302u),
+                      __builtin_amdgcn_perm(b(hi.w), b(hi.z), 0x07060302u)};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// gram_tile for bf16 inputs: the same masked tile from the same LDS rows, on
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16: lane l supplies row l & 15 and
+// the 8 contraction indices 8 (l >> 4) .. + 7 of each operand; the result has
+// the layout of the FP32 16x16x4 product).  Products of bf16 numbers are exact
+// in FP32 and accumulate in FP32, so the tile differs from the FP32 matrix
+// cores' only by the order of the FP32 accumulation; 4 instructions per tile
+// instead of 32.
+template <bool STRICT>
+__device__ __forceinline__ void gram_tile_bf16(PrefillSmem &s, const float *X, float *dst, int tb,
+                                               int sb, int l16, int g) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const float *xa = X + (16 * tb + l16) * LDK + 32 * kk + 8 * g;
+        const float *kb = s.K + (16 * sb + l16) * LDK + 32 * kk + 8 * g;
+        const bf16x8 a = to_bf16x8(lds4(xa), lds4(xa + 4));
+        const bf16x8 b = to_bf16x8(lds4(kb), lds4(kb + 4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g + r, i = 16 * sb + l16;
+        const bool keep = STRICT ? (i < t) : (i <= t);
+        dst[t * LDM + i] = keep ? ratio(s, t, i) * acc[r] : 0.f;
+    }
+}
+
 }  // namespace
 
 // FMT: QRS_FMT_FP32 (0), QRS_FMT_I8F16 (1) or QRS_FMT_U8H16 (2) pool; IN_BF16:
@@ -360,10 +402,17 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             const int tt = tile < 10 ? tile : tile - 10;
             const int tb = tt >= 6 ? 3 : tt >= 3 ? 2 : tt >= 1 ? 1 : 0;
             const int sb = tt - tb * (tb + 1) / 2;
-            if (tile < 10)
-                gram_tile<true>(s, s.K, s.M, tb, sb, l16, g);
-            else
-                gram_tile<false>(s, s.Q, Aqk, tb, sb, l16, g);
+            if (IN_BF16) {   // q and k are exact bf16 numbers: bf16 matrix cores
+                if (tile < 10)
+                    gram_tile_bf16<true>(s, s.K, s.M, tb, sb, l16, g);
+                else
+                    gram_tile_bf16<false>(s, s.Q, Aqk, tb, sb, l16, g);
+            } else {
+                if (tile < 10)
+                    gram_tile<true>(s, s.K, s.M, tb, sb, l16, g);
+                else
+                    gram_tile<false>(s, s.Q, Aqk, tb, sb, l16, g);
+            }
         }
         v4f D[4][2];
 #pragma unroll
