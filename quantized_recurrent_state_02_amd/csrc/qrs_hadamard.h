@@ -59,11 +59,15 @@ __device__ __forceinline__ void hadamard32_pair(float (&x)[16], bool odd) {
                 a[j] = u + v;
                 a[j + h] = u - v;
             }
+    // even lane: u0 + u1 (outputs 0..15); odd lane: u0 - u1 (outputs 16..31),
+    // both as p + sgn a with sgn = +-1: one fma, exact in the product, rounded
+    // once like the add or subtract (a per-lane select cost two more
+    // instructions per value)
+    const double sgn = odd ? -1.0 : 1.0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const double p = partner_f64(a[i]);
-        // even lane: u0 + u1 (outputs 0..15); odd lane: u0 - u1 (outputs 16..31)
-        const double y = odd ? p - a[i] : a[i] + p;
+        const double y = __builtin_fma(a[i], sgn, p);
         x[i] = (float)(y * kInvSqrt32);
     }
 }
@@ -91,9 +95,9 @@ __device__ __forceinline__ void hadamard32_row(float &x0, float &x1, int l16) {
 #define QRS_BFLY(M)                                                        \
     {                                                                      \
         const double pu = row_partner_f64<M>(u, l16), pw = row_partner_f64<M>(w, l16); \
-        const bool up = (l16 >> (M)) & 1;                                  \
-        u = up ? pu - u : u + pu;                                          \
-        w = up ? pw - w : w + pw;                                          \
+        const double sg = ((l16 >> (M)) & 1) ? -1.0 : 1.0;                 \
+        u = __builtin_fma(u, sg, pu);                                      \
+        w = __builtin_fma(w, sg, pw);                                      \
     }
     QRS_BFLY(0)
     QRS_BFLY(1)
