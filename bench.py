@@ -735,6 +735,8 @@ def main():
                     default="all")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--windows", type=int, default=16,
+                    help="whole windows per timed pass of the per-window legs")
     ap.add_argument("--decode-split", choices=["auto", "whole", "halves"], default="auto",
                     help="INT8-tier decode kernel: by grid size (default), one workgroup per "
                          "unit, or two per unit (value-column halves)")
@@ -839,7 +841,7 @@ def main():
                    steps, warmup, args.pools, use_graph, io_bf16=True)
         if args.only in ("window", "all"):
             sec_w, ok_w = run_window(torch, binding, inputs, gdn_in, perm1, c1, n, H, warmup,
-                                     use_graph, warm_s=leg_warm)
+                                     use_graph, reps=args.windows, warm_s=leg_warm)
             window_res = {"workload": f"GDN, {n} slots x {H} heads, windows of {WINDOW} tokens, "
                                       "all slots in phase, 16 windows per timed pass",
                           "us_per_step": sec_w * 1e6, "updates_per_s": n * H / sec_w,
@@ -849,7 +851,7 @@ def main():
                           "finite_outputs": ok_w}
             log(f"[bench] gdn per-window (16): {sec_w * 1e6:.2f} us/step ok={ok_w}")
             sec_s, ok_s = run_window(torch, binding, inputs, gdn_in, perm1, c1, n, H, warmup,
-                                     use_graph, staggered=True, warm_s=leg_warm)
+                                     use_graph, reps=args.windows, staggered=True, warm_s=leg_warm)
             window_res["staggered"] = {
                 "workload": "the same, slot s at position (s + t) mod 16 at step t",
                 "us_per_step": sec_s * 1e6, "updates_per_s": n * H / sec_s,
@@ -858,7 +860,8 @@ def main():
                 "finite_outputs": ok_s}
             log(f"[bench] gdn per-window (16), staggered phases: {sec_s * 1e6:.2f} us/step ok={ok_s}")
             sec_e, ok_e = run_window(torch, binding, inputs, gdn_in, perm1, c1, n, H, warmup,
-                                     use_graph, staggered=True, ends_first=True, warm_s=leg_warm)
+                                     use_graph, reps=args.windows, staggered=True, ends_first=True,
+                                     warm_s=leg_warm)
             window_res["staggered_ends_first"] = {
                 "workload": "the same staggered phases, the batch ordered by descending window "
                             "position at every step (window-end requests first in the grid)",
@@ -875,16 +878,17 @@ def main():
             log(f"[bench] codec comparison: {codec_cmp}")
         del gdn_in
         torch.cuda.empty_cache()
-    if args.only in ("kda", "all"):
+    if args.only in ("kda", "window", "all"):
         perm2 = inputs.protected_perm(2, H)
         c2 = inputs.smoothing(2, H, True)
         kda_in = stage_inputs(torch, inputs, 2, "kda", n, H, total)
-        for pools in sorted({args.pools, 1}, reverse=True):
-            decode(("kda", pools), "kda", binding.FMT_I8F16, kda_in, perm2, c2, n, H, steps,
-                   warmup, pools, use_graph)
-        if args.only == "all":
+        if args.only != "window":
+            for pools in sorted({args.pools, 1}, reverse=True):
+                decode(("kda", pools), "kda", binding.FMT_I8F16, kda_in, perm2, c2, n, H, steps,
+                       warmup, pools, use_graph)
+        if args.only in ("all", "window"):
             sec_k, ok_k = run_window(torch, binding, inputs, kda_in, perm2, c2, n, H, warmup,
-                                     use_graph, kind="kda", warm_s=leg_warm)
+                                     use_graph, reps=args.windows, kind="kda", warm_s=leg_warm)
             kda_window = {
                 "workload": "KDA, 256 slots x 32 heads, windows of 16 tokens, all slots in phase",
                 "us_per_step": sec_k * 1e6, "updates_per_s": n * H / sec_k,
@@ -982,7 +986,8 @@ def main():
         diag("per-window decode: state updates/s (windows of 16 tokens)",
              window_res["updates_per_s"], "state updates/s", window_res["workload"],
              {"bound": "hbm", "achieved": window_res["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-              "frac": window_res["frac_of_peak"], "traffic": None}, {"window": window_res})
+              "frac": window_res["frac_of_peak"], "traffic": None},
+             {"window": window_res, "kda_window": kda_window})
         return
     if not res and select:   # --only select: a diagnostic line for the selection kernels
         diag("key-channel selection: calibration states scored per second",
