@@ -207,18 +207,18 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
  * of section 4.3) on a QRS_FMT_I8F16 pool.  The stored state of a slot stays
  * fixed for `window` tokens (1..32; the pages use 16 and find no gain at 32).  Each token of the
  * window is recorded in a caller-owned update buffer with k and v rounded to
- * FP16 (nearest even) and beta and the decay in FP32 (GDN alpha; KDA the
- * factors exp(g), evaluated once when the token is recorded); the output of token j
+ * FP16 (nearest even), KDA's decay factors exp(g) taken in FP64 and rounded
+ * once to FP16 (nearest even), and beta and GDN's alpha in FP32; the output of token j
  * is that of the FP32 recurrence of qrs_gdn_decode_step / qrs_kda_decode_step
  * started from the dequantized window-start state and run through the
- * window's tokens 0..j (FP16 k and v), read out with this token's q.  The
+ * window's tokens 0..j (their recorded values), read out with this token's q.  The
  * token at position window - 1 writes the requantized end state into the
  * pool, which starts the next window; the others write only their record.
  *   kind: 0 GDN (gate = alpha [n][H]), 1 KDA (gate = g [n][H][128]);
  *   buffer: device memory of >= qrs_window_buffer_bytes(kind, num_slots,
  *     num_heads, window) bytes, 16-byte aligned, laid out as
  *     [num_slots][num_heads][window] records of 528 B (GDN: k FP16[128],
- *     v FP16[128], beta, alpha) or 1,040 B (KDA: k, v, exp(g) FP32[128], beta);
+ *     v FP16[128], beta, alpha) or 784 B (KDA: k, v, exp(g) FP16[128], beta);
  *   pos: int32 [n] device, the index of this token in slot b's window.
  *     Calls must visit positions 0, 1, ..., window - 1 of a slot in order
  *     (position 0 starts from the pool's stored state); a slot id or

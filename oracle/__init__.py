@@ -201,7 +201,8 @@ class OraclePool:
 
     def decode_step(self, slots, q, k, v, gate, beta, kind):
         """One compressed decode step (kind 0 = GDN with alpha [n][H],
-        kind 1 = KDA with log-decay g [n][H][128]); returns o [n][H][128]."""
+        kind 1 = KDA with log-decay g [n][H][128], kind 2 = KDA with the decay
+        factors exp(g) given [n][H][128]); returns o [n][H][128]."""
         slots = _i32(slots)
         q, k, v, gate, beta = (_f32(a) for a in (q, k, v, gate, beta))
         o = np.empty((slots.size, self.num_heads, DV), dtype=np.float32)
@@ -316,14 +317,24 @@ class OracleU8Pool:
         return o
 
 
+def decay_f16(g: np.ndarray) -> np.ndarray:
+    """KDA decay factors of a per-window record: exp(g) in FP64, rounded once
+    to the nearest FP16 (ties to even), as FP32 values.  numpy's float64 ->
+    float16 conversion rounds directly from the double (pinned in
+    tests/test_oracle_window.py against exact rational rounding)."""
+    return np.exp(np.asarray(g, dtype=np.float64)).astype(np.float16).astype(np.float32)
+
+
 class OracleWindowPool:
     """Per-window quantization on the packed pool ("LeapQuant: Efficient Linear
     Attention with Accurate Recurrent State Quantization", section 3.2 and
     Figure 2; memory figures of section 4.3).
 
     The stored (quantized) state of a slot is held fixed for a window of
-    ``window`` tokens.  Every token of the window is recorded with its k and
-    v rounded to FP16 (beta and the gate in FP32), and each output is that of
+    ``window`` tokens.  Every token of the window is recorded as an FP16
+    update: k and v rounded to FP16 and, for KDA, the decay factors exp(g)
+    rounded to FP16 (exp taken in FP64, rounded once to the nearest FP16,
+    ties to even); beta and GDN's alpha stay FP32.  Each output is that of
     the FP32 recurrence started from the dequantized window-start state and
     run through the window's records up to and including the current token,
     read out with the current q.  The token that completes the window stores
@@ -353,11 +364,13 @@ class OracleWindowPool:
             assert len(recs) == int(pos[b]), "window positions must advance one token at a time"
             k16 = f16_bits_to_f32(f32_to_f16_bits(k[b]))
             v16 = f16_bits_to_f32(f32_to_f16_bits(v[b]))
-            recs.append((k16, v16, gate[b].copy(), beta[b].copy()))
+            recs.append((k16, v16, decay_f16(gate[b]) if kind == 1 else gate[b].copy(),
+                         beta[b].copy()))
             dense = OracleDensePool(1, H, self.pool.perm, self.pool.c)
             dense.T[:] = self.pool.dequant([s], space=1)[0]
+            rkind = 2 if kind == 1 else kind    # KDA records hold the decay factors
             for kk, vv, gg, bb in recs:
-                o = dense.decode_step([0], q[b:b + 1], kk[None], vv[None], gg[None], bb[None], kind)
+                o = dense.decode_step([0], q[b:b + 1], kk[None], vv[None], gg[None], bb[None], rkind)
             out[b] = o[0]
             if len(recs) == self.window:
                 self.pool.store([s], dense.T.reshape(1, H, DK, DV), space=1)

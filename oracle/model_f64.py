@@ -8,7 +8,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
     S_t = A_t S_{t-1} + beta_t k_t v_t^T,   A_t = (I - beta_t k_t k_t^T) Lambda_t,
     o_t = S_t^T q_t,
 
-with Lambda_t = alpha_t I for GDN and diag(exp(g_t)) for KDA.  This is written
+with Lambda_t = alpha_t I for GDN (kind 0), diag(exp(g_t)) for KDA (kind 1),
+and diag(lambda_t) for KDA with the decay factors given (kind 2).  This is written
 with an explicit transition matrix and numpy matrix products, independently
 of the delta form used by the C oracle, so that the two pin each other.
 
@@ -26,8 +27,10 @@ def transition(k, gate, beta, kind):
     d = k.shape[0]
     if kind == 0:
         lam = np.full(d, float(gate))
-    else:
+    elif kind == 1:
         lam = np.exp(np.asarray(gate, dtype=np.float64))
+    else:
+        lam = np.asarray(gate, dtype=np.float64)
     return (np.eye(d) - float(beta) * np.outer(k, k)) @ np.diag(lam)
 
 

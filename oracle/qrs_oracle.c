@@ -300,7 +300,10 @@ static void step_unit_f64(const double *Th, double *T, const double *lam, const 
 }
 
 /* Gather the per-step operands of unit (b, h) into stored key order.
- * kind 0: GDN, gate = alpha [n][H]; kind 1: KDA, gate = g [n][H][DK]. */
+ * kind 0: GDN, gate = alpha [n][H]; kind 1: KDA, gate = g [n][H][DK]
+ * (Lambda = diag(exp(g)), HTML section 3.1); kind 2: KDA with the decay
+ * factors exp(g) given directly, gate = lambda [n][H][DK] (the per-window
+ * method's recorded decays). */
 static void gather_operands(int kind, int b, int h, int num_heads, const int32_t *perm,
                             const float *c, const float *q, const float *k, const float *v,
                             const float *gate, float *qp, float *kp, float *vp, float *lam)
@@ -310,7 +313,9 @@ static void gather_operands(int kind, int b, int h, int num_heads, const int32_t
         int src = perm[h * DK + i];
         qp[i] = q[base + src];
         kp[i] = k[base + src];
-        lam[i] = kind == 0 ? gate[(int64_t)b * num_heads + h] : expf(gate[base + src]);
+        lam[i] = kind == 0   ? gate[(int64_t)b * num_heads + h]
+                 : kind == 1 ? expf(gate[base + src])
+                             : gate[base + src];
     }
     for (int j = 0; j < DV; ++j)
         vp[j] = v[base + j] / c[h * DV + j];                      /* v' = D_c^{-1} v */
@@ -378,7 +383,9 @@ void orc_f64_decode(double *Tpool, int num_heads, const int32_t *perm, const flo
             int src = perm[h * DK + i];
             qp[i] = q[base + src];
             kp[i] = k[base + src];
-            lam[i] = kind == 0 ? (double)gate[uu] : exp((double)gate[base + src]);
+            lam[i] = kind == 0   ? (double)gate[uu]
+                     : kind == 1 ? exp((double)gate[base + src])
+                                 : (double)gate[base + src];
         }
         for (int j = 0; j < DV; ++j) {
             cc[j] = c[h * DV + j];

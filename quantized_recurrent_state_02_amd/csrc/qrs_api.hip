@@ -12,6 +12,7 @@
 
 #include "../../include/qrs.h"
 #include "qrs_internal.h"
+#include "qrs_window.h"
 
 namespace qrs {
 hipError_t launch_decode_half(int kind, int io, const PoolView &pool, const int32_t *slots, int n,
@@ -289,7 +290,7 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
 size_t qrs_window_buffer_bytes(int kind, int num_slots, int num_heads, int window) {
     if ((kind != 0 && kind != 1) || num_slots <= 0 || num_heads <= 0 || window < 1 || window > 32)
         return 0;
-    const size_t rec = kind == 0 ? 528 : 1040;
+    const size_t rec = (size_t)qrs::window_record_bytes(kind);
     const size_t units = (size_t)num_slots * (size_t)num_heads;
     if (units > ((size_t)1 << 40) / (rec * (size_t)window)) return 0;
     return units * (size_t)window * rec;

@@ -22,22 +22,38 @@
 // Record of token t of slot s, head h, at buffer + ((s H + h) window + t) R:
 //   [0, 256) k FP16 [128], [256, 512) v FP16 [128] (model order);
 //   GDN (R = 528): [512] beta, [516] alpha (FP32);
-//   KDA (R = 1040): [512, 1024) exp(g) FP32 [128], [1024] beta.
-// The KDA record holds the decay factors exp(g) rather than g: exp runs once,
-// when the token is recorded, instead of at every later use (the query's
-// back-propagation through the window and the window-end replay), and the
-// values used are the same.
+//   KDA (R = 784): [512, 768) the decay factors exp(g) FP16 [128], [768] beta.
+// The record is the token's update in FP16 (LeapQuant's FP16 update buffer):
+// k, v and, for KDA, exp(g) taken in FP64 and rounded once to FP16 (ties to
+// even), evaluated when the token is recorded; beta and GDN's alpha stay FP32.
 #include "qrs_internal.h"
+#include "qrs_window.h"
 
 namespace qrs {
 
 constexpr int WIN_MAX = 32;
 
-__host__ __device__ constexpr int window_record_bytes(int kind) { return kind == 0 ? 528 : 1040; }
 
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// A KDA decay factor as recorded: exp(g) in FP64, rounded once to FP16 (ties
+// to even).  The FP64 value is first rounded to FP32 with round-to-odd (the
+// nearest-even FP32 value, moved one step toward zero and made odd when it is
+// inexact and above), then FP32 -> FP16 rounds to nearest even; with 13 more
+// bits in FP32 than in FP16 the two steps equal one correct rounding.
+// Returns the FP16 bits.
+__device__ __forceinline__ uint32_t decay_f16_bits(float g) {
+    const double e = exp((double)g);  // in [0, 1] for g <= 0
+    const float t = (float)e;
+    uint32_t u = __builtin_bit_cast(uint32_t, t);
+    if ((double)t != e) {
+        if ((double)t > e) u -= 1u;  // e >= 0, so t > e >= 0 and u >= 1
+        u |= 1u;
+    }
+    return f32_to_f16_bits(__builtin_bit_cast(float, u));
+}
 
 // Fields of a record staged in LDS (the record layout, byte offsets).
 __device__ __forceinline__ float lds_f16(const uint8_t *base, int byte_off) {
@@ -63,7 +79,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     const float *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta,
     float *__restrict__ o) {
     constexpr int R = window_record_bytes(KIND);
-    constexpr int BOFF = KIND == 0 ? 512 : 1024;  // beta's byte offset in a record
+    constexpr int BOFF = KIND == 0 ? 512 : 768;  // beta's byte offset in a record
     // 16-byte pieces of the earlier records that one thread stages (at most
     // WIN_MAX - 1 records precede a token)
     constexpr int NCH = ((WIN_MAX - 1) * (R / 16) + THREADS - 1) / THREADS;
@@ -118,7 +134,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     const float beta_c = beta[uu];
     const float alpha_c = KIND == 0 ? gate[uu] : 0.f;
     const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
-    const float lam_c = KIND == 1 ? expf(g_c) : 0.f;   // this token's decay of key channel tid
+    // this token's decay of key channel tid as recorded (FP16), KDA
+    const uint32_t lam16 = KIND == 1 ? decay_f16_bits(g_c) : 0u;
+    const float lam_c = f16_bits_to_f32(lam16);
     U4 hi_raw[2];
     U4 lo_raw[ROWS_PER_THREAD - 1];
     float sc_old[ROWS_PER_THREAD - 1];
@@ -142,7 +160,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     if (!boundary) {
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k16, rb, p * R + 2 * tid, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v16, rb, p * R + 256 + 2 * tid, 0, 0);
-        if (KIND == 1) buf_storef(rb, lam_c, p * R + 512 + 4 * tid, 0);
+        if (KIND == 1)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)lam16, rb, p * R + 512 + 2 * tid, 0, 0);
         if (tid == 0) {
             buf_storef(rb, beta_c, p * R + BOFF, 0);
             if (KIND == 0) buf_storef(rb, alpha_c, p * R + 516, 0);
@@ -169,8 +188,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
                 const uint8_t *rec = s_rec + (t > 0 ? t - 1 : 0) * R;
                 const float nka = lds_f16(rec, 2 * m0), nkb = lds_f16(rec, 2 * m1);
                 const float nbt = lds_f32(rec, BOFF);
-                const float nla = KIND == 0 ? lds_f32(rec, 516) : lds_f32(rec, 512 + 4 * m0);
-                const float nlb = KIND == 0 ? nla : lds_f32(rec, 512 + 4 * m1);
+                const float nla = KIND == 0 ? lds_f32(rec, 516) : lds_f16(rec, 512 + 2 * m0);
+                const float nlb = KIND == 0 ? nla : lds_f16(rec, 512 + 2 * m1);
                 const float coef = bt * wave_allsum(__builtin_fmaf(ka, x0, kb * x1));
                 if (tid == 0) s_coef[t] = coef;
                 x0 = la * (x0 - coef * ka);
@@ -282,7 +301,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
             for (int r = 0; r < ROWS_PER_THREAD; ++r) {
                 const int m = s_perm[rg + 16 * r];
                 kr[r] = lds_f16(rec, 2 * m);
-                dr[r] = KIND == 0 ? at : lds_f32(rec, 512 + 4 * m);
+                dr[r] = KIND == 0 ? at : lds_f16(rec, 512 + 2 * m);
             }
             ka[0] = lds_f16(rec, 2 * ma[0]);
             ka[1] = lds_f16(rec, 2 * ma[1]);

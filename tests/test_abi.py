@@ -166,7 +166,7 @@ def test_decode_step_ex_rejects_null_pool(lib):
 def test_window_buffer_bytes_and_null_pool(lib):
     f = lib.qrs_window_buffer_bytes
     assert f(0, 4, 32, 16) == 4 * 32 * 16 * 528      # GDN record: k, v FP16 + beta, alpha
-    assert f(1, 4, 32, 16) == 4 * 32 * 16 * 1040     # KDA record: k, v FP16 + g FP32 + beta
+    assert f(1, 4, 32, 16) == 4 * 32 * 16 * 784      # KDA record: k, v, exp(g) FP16 + beta, padded to 16 B
     assert f(0, 4, 32, 16) // (4 * 32) < 8.5 * 1024  # about 8 KiB per head at window 16
     for bad in ((2, 4, 32, 16), (0, 0, 32, 16), (0, 4, 0, 16), (0, 4, 32, 0), (0, 4, 32, 33)):
         assert f(*bad) == 0

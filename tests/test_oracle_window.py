@@ -1,6 +1,9 @@
 """Pins of the per-window quantization oracle (oracle.OracleWindowPool;
 "LeapQuant: Efficient Linear Attention with Accurate Recurrent State
 Quantization", section 3.2, Figure 2, section 4.3)."""
+import math
+from fractions import Fraction
+
 import numpy as np
 
 import oracle
@@ -24,9 +27,78 @@ def _setup(H, n, window, seed=0):
     return wp, perm, c, S0, slots
 
 
+def _f16_exact(x: float) -> float:
+    """The FP16 number nearest to the double x (ties to even), by exact
+    rational arithmetic: the reference for the record's decay rounding."""
+    if x == 0.0:
+        return 0.0
+    fx = Fraction(x)
+    best = None
+    e = max(math.frexp(abs(x))[1] - 11, -24)      # spacing 2^e of FP16 numbers near |x|
+    q = abs(fx) / Fraction(2) ** e
+    lo = math.floor(q)
+    for m in (lo, lo + 1):
+        cand = Fraction(m) * Fraction(2) ** e
+        dist = abs(abs(fx) - cand)
+        if best is None or dist < best[0] or (dist == best[0] and m % 2 == 0):
+            best = (dist, cand)
+    v = float(best[1])
+    return math.copysign(min(v, 65504.0) if v <= 65520.0 else math.inf, x)
+
+
+def test_f64_to_f16_rounding_of_the_record_decays():
+    """The KDA record's decay factors: exp(g) in FP64 rounded once to FP16.
+    numpy's float64 -> float16 conversion is checked against exact rounding
+    at FP16 midpoints (ties to even), one FP64 ulp either side of them, and
+    on the workload's decays; decay_f16 against exact rounding of math.exp."""
+    r = np.random.default_rng(7)
+    h = np.sort(np.unique(r.integers(1, 0x7BFF, 4000).astype(np.uint16))).view(np.float16)
+    h = h.astype(np.float64)
+    mids = (h[:-1] + np.nextafter(h[:-1].astype(np.float16), np.float16(np.inf)).astype(np.float64)) / 2
+    cases = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)])
+    got = cases.astype(np.float16).astype(np.float64)
+    for x, y in zip(cases.tolist(), got.tolist()):
+        assert y == _f16_exact(x), x
+    g = -np.logaddexp(0.0, r.standard_normal(3000) + 2.0).astype(np.float32)
+    g = np.concatenate([g, np.float32([0.0, -np.inf, -20.0, -9.9, -1e-8])])
+    lam = oracle.decay_f16(g)
+    for gi, li in zip(g.tolist(), lam.tolist()):
+        assert li == _f16_exact(math.exp(gi)), gi
+
+
+def test_kind2_is_kda_with_given_decays():
+    """kind 2 (decay factors given) against the other kinds: with every factor
+    equal to alpha it is GDN bit for bit (dense FP32 and compressed steps);
+    in the FP64 twin, factors exp(g) give kind 1's result."""
+    H, n = 2, 2
+    perm = inputs.protected_perm(2, H)
+    c = inputs.smoothing(2, H, True)
+    slots = np.arange(n, dtype=np.int32)
+    S0 = inputs.initial_state(2, n, H)
+    d = inputs.step_inputs(2, 0, n, H, "kda")
+    a = np.full((n, H), 0.375, np.float32)
+    lam = np.repeat(a[..., None], DK, axis=2)
+    for P in (oracle.OracleDensePool, oracle.OraclePool):
+        p0, p2 = P(n, H, perm, c), P(n, H, perm, c)
+        if P is oracle.OracleDensePool:
+            p0.set_model(slots, S0); p2.set_model(slots, S0)
+        else:
+            p0.store(slots, S0); p2.store(slots, S0)
+        o0 = p0.decode_step(slots, d["q"], d["k"], d["v"], a, d["beta"], 0)
+        o2 = p2.decode_step(slots, d["q"], d["k"], d["v"], lam, d["beta"], 2)
+        assert np.array_equal(o0, o2)
+    q1, q2 = (oracle.OracleDensePool(n, H, perm, c, dtype=np.float64) for _ in range(2))
+    q1.set_model(slots, S0); q2.set_model(slots, S0)
+    o1 = q1.decode_step(slots, d["q"], d["k"], d["v"], d["g"], d["beta"], 1)
+    o2 = q2.decode_step(slots, d["q"], d["k"], d["v"], np.exp(d["g"].astype(np.float64)).astype(np.float32),
+                        d["beta"], 2)
+    # exp rounded to FP32 in the kind-2 input: differences at FP32 level only
+    assert np.abs(o1 - o2).max() <= 1e-6 * np.abs(o1).max()
+
+
 def test_window_one_is_the_per_step_method():
     """Window 1: every token is the per-step compressed decode with k and v
-    rounded to FP16 -- bit for bit."""
+    rounded to FP16 (KDA: with the FP16-rounded decay factors) -- bit for bit."""
     H, n = 3, 2
     wp, perm, c, S0, slots = _setup(H, n, 1)
     ref = oracle.OraclePool(n, H, perm, c)
@@ -35,7 +107,12 @@ def test_window_one_is_the_per_step_method():
         for kind, cfg, key in ((0, 1, "alpha"), (1, 2, "g")):
             d = inputs.step_inputs(cfg, t, n, H, "gdn" if kind == 0 else "kda")
             o = wp.step(slots, np.zeros(n, np.int32), d["q"], d["k"], d["v"], d[key], d["beta"], kind)
-            o2 = ref.decode_step(slots, d["q"], _f16(d["k"]), _f16(d["v"]), d[key], d["beta"], kind)
+            if kind == 0:
+                o2 = ref.decode_step(slots, d["q"], _f16(d["k"]), _f16(d["v"]), d[key], d["beta"], 0)
+            else:
+                lam16 = np.vectorize(lambda x: _f16_exact(math.exp(x)))(d[key].astype(np.float64))
+                o2 = ref.decode_step(slots, d["q"], _f16(d["k"]), _f16(d["v"]),
+                                     lam16.astype(np.float32), d["beta"], 2)
             assert np.array_equal(o, o2)
             assert np.array_equal(wp.pool.lo, ref.lo) and np.array_equal(wp.pool.sc, ref.sc)
             assert np.array_equal(wp.pool.hi, ref.hi)
@@ -44,7 +121,8 @@ def test_window_one_is_the_per_step_method():
 def test_state_fixed_inside_a_window_and_outputs_are_the_exact_recurrence():
     """Inside a window the stored bytes do not change; every output equals
     the FP64 recurrence (product form, model coordinates) from the dequantized
-    window-start state through the FP16-rounded tokens, to FP32 accuracy."""
+    window-start state through the FP16-rounded tokens (k, v and the decay
+    factors), to FP32 accuracy."""
     H, n, p = 2, 2, 8
     wp, perm, c, S0, slots = _setup(H, n, p)
     start = wp.pool.dequant(slots).astype(np.float64)
@@ -54,11 +132,12 @@ def test_state_fixed_inside_a_window_and_outputs_are_the_exact_recurrence():
         d = inputs.step_inputs(2, t, n, H, "kda")
         o = wp.step(slots, np.full(n, t, np.int32), d["q"], d["k"], d["v"], d["g"], d["beta"], 1)
         k16, v16 = _f16(d["k"]), _f16(d["v"])
+        lam16 = np.exp(d["g"].astype(np.float64)).astype(np.float16).astype(np.float64)
         o_ref = np.empty((n, H, DV))
         for b in range(n):
             for h in range(H):
                 S[b, h], o_ref[b, h], _ = model_f64.step(S[b, h], d["q"][b, h], k16[b, h], v16[b, h],
-                                                         d["g"][b, h], d["beta"][b, h], 1)
+                                                         lam16[b, h], d["beta"][b, h], 2)
         rel = np.abs(o - o_ref).max() / np.abs(o_ref).max()
         assert rel < 2e-5, (t, rel)
         if t < p - 1:
@@ -97,5 +176,7 @@ def test_fewer_requantizations_track_the_reference_more_closely():
 
 def test_update_buffer_size():
     """Section 4.3: the FP16 update buffer of a 16-token window is about 8 KiB
-    per head for 128 x 128 states (16 tokens x (k + v) x 128 x 2 bytes)."""
+    per head for 128 x 128 states (16 tokens x (k + v) x 128 x 2 bytes); KDA's
+    records add the 128 FP16 decay factors."""
     assert 16 * 2 * 128 * 2 == 8 * 1024
+    assert 2 * 128 * 2 + 128 * 2 + 4 <= 784 == 49 * 16
