@@ -63,6 +63,8 @@ BYTES_GDN_BF16IO = 20224 * 2 + 3 * 256 + 8
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gdn_b256_h32_counters.json")
 TRACE_FILE = os.path.join(ROOT, "profiles", "decode_gdn_b256_h32_kernel_trace.json")
 KERNEL_SOURCES = ["quantized_recurrent_state_02_amd/csrc/qrs_decode.hip",
+                  "quantized_recurrent_state_02_amd/csrc/qrs_decode_half.h",
+                  "quantized_recurrent_state_02_amd/csrc/qrs_hadamard.h",
                   "quantized_recurrent_state_02_amd/csrc/qrs_internal.h"]
 
 

@@ -345,11 +345,14 @@ int qrs_select_protected_channels(int num_heads, const double *score_host, int k
  *   QRS_DECODE_SPLIT_HALVES: two workgroups per unit, for grids too small to
  *     fill the GPU (a whole-unit workgroup's lifetime then sets the step);
  *   QRS_DECODE_SPLIT_AUTO (the default): the halves below 1,024 units per call
- *     (n * head count); on MI355X they are faster only there.
+ *     (n * head count), where on MI355X they are faster; above, whole units,
+ *     and for grids of more than two generations of resident workgroups the
+ *     last eighth of a generation's units as halves, at the end of the same
+ *     launch, which shortens its drain.
  * The setting is process-wide, applies to calls enqueued after it returns,
  * and is a tuning choice only.  Returns the previous mode (>= 0), or
- * QRS_EINVAL for another value (the setting is then unchanged).  Other pool formats and the
- * per-window step ignore it.
+ * QRS_EINVAL for another value (the setting is then unchanged).  Other pool
+ * formats and the per-window step ignore it.
  */
 enum {
     QRS_DECODE_SPLIT_AUTO = 0,

@@ -21,7 +21,7 @@ hipError_t launch_decode_half(int kind, int io, const PoolView &pool, const int3
 hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &pool,
                                 const int32_t *slots, int n, int h0, int hc, const void *q,
                                 const void *k, const void *v, const float *gate, const float *beta,
-                                void *o, hipStream_t stream);
+                                void *o, bool half_tail, hipStream_t stream);
 hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n, int h0,
                              int hc, const float *q, const float *k, const float *v,
                              const float *gate, const float *beta, float *o, hipStream_t stream);
@@ -120,7 +120,9 @@ struct DeviceGuard {
 
 // Which INT8-tier decode kernel runs: one workgroup per unit, or two per unit
 // (value-column halves) for grids too small to fill the GPU.
-// QRS_DECODE_SPLIT_AUTO picks the halves below kDecodeSplitUnits units.
+// QRS_DECODE_SPLIT_AUTO picks the halves below kDecodeSplitUnits units, and
+// above lets the whole-unit kernel end a large grid with half-unit
+// workgroups; QRS_DECODE_SPLIT_WHOLE uses whole-unit workgroups only.
 std::atomic<int> g_decode_split{QRS_DECODE_SPLIT_AUTO};
 constexpr int kDecodeSplitUnits = 1024;
 
@@ -149,8 +151,10 @@ int decode_common(int kind, int io, qrs_pool pool, const int32_t *slots, int n, 
                                      gate, beta, static_cast<float *>(o), stream)
         : pool->fmt == QRS_FMT_I8F16 && use_half_kernel(n * hc)
             ? qrs::launch_decode_half(kind, io, pv, slots, n, h0, hc, q, k, v, gate, beta, o, stream)
-            : qrs::launch_decode_packed(kind, pool->fmt == QRS_FMT_U8H16 ? 1 : 0, io, pv, slots, n,
-                                        h0, hc, q, k, v, gate, beta, o, stream);
+            : qrs::launch_decode_packed(
+                  kind, pool->fmt == QRS_FMT_U8H16 ? 1 : 0, io, pv, slots, n, h0, hc, q, k, v, gate,
+                  beta, o,
+                  g_decode_split.load(std::memory_order_relaxed) == QRS_DECODE_SPLIT_AUTO, stream);
     return e == hipSuccess ? QRS_OK : QRS_EDEVICE;
 }
 

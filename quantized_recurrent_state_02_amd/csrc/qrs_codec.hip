@@ -97,13 +97,10 @@ __global__ __launch_bounds__(THREADS) void store_packed_kernel(PoolView pool,
                 hi = fmaxf(hi, x[r][c]);
             }
             const U8Params pr = u8_params(lo, hi);
-            float q[COLS_PER_THREAD];
-#pragma unroll
-            for (int c = 0; c < COLS_PER_THREAD; ++c) q[c] = u8_code(x[r][c], pr);
-            cw.x = pack4_u8(q[0], q[1], q[2], q[3]);
-            cw.y = pack4_u8(q[4], q[5], q[6], q[7]);
-            cw.z = pack4_u8(q[8], q[9], q[10], q[11]);
-            cw.w = pack4_u8(q[12], q[13], q[14], q[15]);
+            cw.x = u8_pack4(x[r][0], x[r][1], x[r][2], x[r][3], pr);
+            cw.y = u8_pack4(x[r][4], x[r][5], x[r][6], x[r][7], pr);
+            cw.z = u8_pack4(x[r][8], x[r][9], x[r][10], x[r][11], pr);
+            cw.w = u8_pack4(x[r][12], x[r][13], x[r][14], x[r][15], pr);
             meta = pr.meta;
         }
         *reinterpret_cast<V4 *>(unit + LO_OFF + lrow * DV + cb * 16) = cw;

@@ -33,6 +33,7 @@
 // single 16-byte scale accesses all measured the same or slower.
 #include <atomic>
 
+#include "qrs_decode_half.h"
 #include "qrs_hadamard.h"
 
 namespace qrs {
@@ -42,8 +43,11 @@ namespace qrs {
 // revision's tier (block-32 Hadamard, asymmetric UINT8, FP16 scale and zero
 // point; qrs_hadamard.h), read and written at the same offsets.
 // IO 0: q, k, v, o in FP32; IO 1: in bf16 (gates and beta stay FP32).
-// Workgroup i handles slot b = i / hc, head h0 + i % hc; operands and
-// outputs are indexed [n][H] as for the full head range.
+// Workgroup i < nwhole handles unit i (slot b = i / hc, head h0 + i % hc);
+// operands and outputs are indexed [n][H] as for the full head range.  The
+// INT8 tier may end its grid with half-unit workgroups (i >= nwhole, two per
+// unit, qrs_decode_half.h) for units nwhole .. units - 1: they live about
+// half as long, so the launch drains sooner (the launcher below).
 // The INT8 tier is held to 168 VGPRs, three waves per SIMD (six units per
 // CU); at 180 VGPRs it ran two waves per SIMD and was 3-4% slower.  The
 // first revision's tier needs about 200 VGPRs for its transforms and stays
@@ -58,8 +62,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((
     amdgpu_waves_per_eu(DecodeOccupancy<CODEC>::waves, DecodeOccupancy<CODEC>::waves))) void
 decode_packed_kernel(
     PoolView pool, const int32_t *__restrict__ slots, int first_gen, int n_cus, int h0, int hc,
-    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
-    const float *__restrict__ gate, const float *__restrict__ beta, void *__restrict__ o) {
+    int nwhole, int units, const void *__restrict__ q, const void *__restrict__ k,
+    const void *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta, void *__restrict__ o) {
     __shared__ float s_k[DK];
     __shared__ float s_q[DK];
     __shared__ float s_dec[DK];
@@ -72,6 +76,13 @@ decode_packed_kernel(
     __shared__ float4 red_w[16][DV / 4];
     __shared__ float4 red_z[16][DV / 4];
 
+    if (CODEC == 0 && (int)blockIdx.x >= nwhole) {
+        const HalfLds L{s_k,    s_q,    s_dec, s_bd,         s_vp,        s_kraw,
+                        s_qraw, s_graw, s_qk,  &red_w[0][0], &red_z[0][0]};
+        decode_half_unit<KIND, IO>(pool, slots, units, h0, hc, (int)blockIdx.x - nwhole, nwhole, q,
+                                   k, v, gate, beta, o, L);
+        return;
+    }
     // Staggered start of the first generation (the workgroups resident at
     // launch; first_gen = 0 when the grid is too small to benefit): the j-th
     // workgroup placed on each CU waits j x 2048 cycles (~0.85 us), so the
@@ -180,11 +191,29 @@ decode_packed_kernel(
             x[0][2 * c + 1] = mul_f16hi(dr[0], hw[c]);
         }
     }
+    // first revision's tier: the integer inverse transform when every group
+    // of the wave is in its exact range (a wave-uniform choice), else FP64
+    bool v1_int = false;
+    if (CODEC == 1) {
+        bool ok = true;
+#pragma unroll
+        for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+            const uint32_t m = __builtin_bit_cast(uint32_t, sc_old[r - 1]);
+            ok = ok && u8_group_exact(f16_bits_to_f32(m & 0xffffu), f16_bits_to_f32(m >> 16));
+        }
+        v1_int = __builtin_amdgcn_ballot_w64(!ok) == 0;
+    }
 #pragma unroll
     for (int r = 1; r < ROWS_PER_THREAD; ++r) {
         const uint32_t lw[4] = {lo_raw[r - 1].x, lo_raw[r - 1].y, lo_raw[r - 1].z,
                                 lo_raw[r - 1].w};
-        if (CODEC == 0) {
+        if (CODEC == 1 && v1_int) {
+            const uint32_t m = __builtin_bit_cast(uint32_t, sc_old[r - 1]);
+            const float sh = f16_bits_to_f32(m & 0xffffu), zh = f16_bits_to_f32(m >> 16);
+            hadamard32_pair_codes(lw, sh, zh, (cb & 1) != 0, x[r]);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) x[r][c] = dr[r] * x[r][c];
+        } else if (CODEC == 0) {
             const float a = dr[r] * sc_old[r - 1];
 #pragma unroll
             for (int c = 0; c < 16; ++c) x[r][c] = a * sext_byte_to_f32(lw[c >> 2], c & 3);
@@ -303,13 +332,10 @@ decode_packed_kernel(
                 hi = fmaxf(hi, x[r][c]);
             }
             const U8Params pr = u8_params(lo, hi);
-            float q[COLS_PER_THREAD];
-#pragma unroll
-            for (int c = 0; c < COLS_PER_THREAD; ++c) q[c] = u8_code(x[r][c], pr);
-            cw.x = pack4_u8(q[0], q[1], q[2], q[3]);
-            cw.y = pack4_u8(q[4], q[5], q[6], q[7]);
-            cw.z = pack4_u8(q[8], q[9], q[10], q[11]);
-            cw.w = pack4_u8(q[12], q[13], q[14], q[15]);
+            cw.x = u8_pack4(x[r][0], x[r][1], x[r][2], x[r][3], pr);
+            cw.y = u8_pack4(x[r][4], x[r][5], x[r][6], x[r][7], pr);
+            cw.z = u8_pack4(x[r][8], x[r][9], x[r][10], x[r][11], pr);
+            cw.w = u8_pack4(x[r][12], x[r][13], x[r][14], x[r][15], pr);
             meta = __builtin_bit_cast(float, pr.meta);
         }
         buf_store16(st, cw, off_lo2, LO_OFF + 2048 * (r - 1));
@@ -343,21 +369,31 @@ static void decode_residency(int *per_cu, int *cus) {
     *per_cu = p;
     *cus = c;
 }
-// The stagger pays off only when later generations follow the first.
+// The stagger pays off only when later generations follow the first, and so
+// does the half-unit tail: when the grid holds more than two generations of
+// resident workgroups (INT8 tier, half_tail set), the last resident / 8 units
+// (a multiple of 8) run as value-column halves.  On MI355X at batch 256 x 32
+// heads (6 x 256 resident) this took 0.5-0.7 us off a 60.5 us step for GDN and
+// KDA on two boxes (tails of 192, 256 and 384 units within noise of each
+// other; 512 gained less, 1,536 lost 1.5 us).
 #define QRS_DECODE_CASE(K, C, I)                                                                  \
     if (kind == K && codec == C && io == I) {                                                     \
         int per_cu = 0, cus = 1;                                                                  \
         decode_residency<K, C, I>(&per_cu, &cus);                                                 \
-        const int first_gen = n * hc > 2 * per_cu * cus ? per_cu * cus : 0;                      \
+        const int units = n * hc, resident = per_cu * cus;                                        \
+        const bool big = units > 2 * resident;                                                    \
+        const int first_gen = big ? resident : 0;                                                 \
+        const int tail = C == 0 && half_tail && big ? (resident / 8) & ~7 : 0;                    \
+        const int nwhole = units - tail;                                                          \
+        dim3 grid((unsigned)(nwhole + 16 * ((tail + 7) / 8))), block(THREADS);                    \
         hipLaunchKernelGGL((decode_packed_kernel<K, C, I>), grid, block, 0, stream, pool, slots,  \
-                           first_gen, cus, h0, hc, q, k, v, gate, beta, o);                       \
+                           first_gen, cus, h0, hc, nwhole, units, q, k, v, gate, beta, o);        \
         return hipGetLastError();                                                                 \
     }
 hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &pool,
                                 const int32_t *slots, int n, int h0, int hc, const void *q,
                                 const void *k, const void *v, const float *gate, const float *beta,
-                                void *o, hipStream_t stream) {
-    dim3 grid((unsigned)(n * hc)), block(THREADS);
+                                void *o, bool half_tail, hipStream_t stream) {
     QRS_DECODE_CASE(0, 0, 0)
     QRS_DECODE_CASE(1, 0, 0)
     QRS_DECODE_CASE(0, 1, 0)

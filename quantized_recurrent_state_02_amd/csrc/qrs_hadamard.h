@@ -108,6 +108,87 @@ __device__ __forceinline__ void hadamard32_row(float &x0, float &x1, int l16) {
     x1 = (float)(w * kInvSqrt32);
 }
 
+// ---- the inverse transform of a stored group from its codes ----
+//
+// A stored group reconstructs as y_i = RN32(s16 (q_i - z16)) (Eq.(3)) and
+// transforms back as RN32(RN64(2^-2.5) * sum_j H[i][j] y_j) with the sums in
+// FP64.  When 0 < s16 <= 65504 and -7936 <= z16 <= 8191, every |q_i - z16| is
+// below 2^13, so with the 11 significant bits of s16 each y_i is an exact
+// FP32 product s16 m_i, every partial sum is s16 times an integer below 2^18
+// (exact in FP64, in any order), and the sum is s16 (H q)_i - 32 z16 s16
+// [i = 0] (only the first row of H has a nonzero sum).  H q, with |(H q)_i|
+// <= 32 * 255, is computed on packed 16-bit integers; for i != 0, t =
+// s16 (H q)_i is again an exact FP32 product, and RN32(RN64(c t)) for c =
+// RN64(2^-2.5) equals fma(t, c_hi, RN32(t c_lo)) with c_hi = RN32(c), c_lo =
+// RN32(c - c_hi) for every FP32 t whose products stay normal (an exhaustive
+// check over all 2^23 significands; the test suite repeats it); the output
+// with the z16 term takes the FP64 path.  Same bits as hadamard32_pair on
+// the reconstruction, in about 8 instead of 13 VALU instructions per value.
+// A zero scale takes the FP64 path (there a negative integer sum would give
+// -0 for the +0 of the definition).
+
+// A stored group (FP16 s16, z16 as FP32) inside the exact range above.
+__device__ __forceinline__ bool u8_group_exact(float sh, float zh) {
+    return sh > 0.0f && sh <= 65504.0f && zh >= -7936.0f && zh <= 8191.0f;
+}
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// RN64(2^-2.5) as an unevaluated FP32 sum.
+constexpr float kInvSqrt32Hi = 0x1.6a09e6p-3f;
+constexpr float kInvSqrt32Lo = 0x1.9fcef4p-29f;
+
+// x (this lane's 16 outputs, positions 16 odd .. + 15 of the group) from the
+// lane's 16 codes (bytes of lw, position c in byte c & 3 of lw[c >> 2]) and
+// the group's s16, z16, for a group with u8_group_exact(sh, zh).  Register
+// P[j] holds positions j (low half) and j + 8 (high half).
+__device__ __forceinline__ void hadamard32_pair_codes(const uint32_t (&lw)[4], float sh, float zh,
+                                                      bool odd, float (&x)[16]) {
+    s16x2 P[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)  // bytes j and j + 8, zero-extended to 16 bits
+        P[j] = __builtin_bit_cast(
+            s16x2, __builtin_amdgcn_perm(lw[(j >> 2) + 2], lw[j >> 2],
+                                         0x0C040C00u + (uint32_t)(j & 3) * 0x00010001u));
+    // H_16 in the lane: position bits 0..2 across registers, bit 3 across halves
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if ((j & h) == 0) {
+                const s16x2 u = P[j], v = P[j + h];
+                P[j] = u + v;
+                P[j + h] = u - v;
+            }
+    const s16x2 pm = {1, -1};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) P[j] = P[j].xx + P[j].yy * pm;
+    // H_2 across the lane pair: even lane u0 + u1, odd lane u0 - u1.  The
+    // sign is opaque to the compiler, so the product stays one packed
+    // multiply-add instead of a negate, a select and an add.
+    uint32_t sgw = odd ? 0xffffffffu : 0x00010001u;
+    asm volatile("" : "+v"(sgw));
+    const s16x2 sg = __builtin_bit_cast(s16x2, sgw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const s16x2 p = __builtin_bit_cast(
+            s16x2, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, P[j]), 0xB1, 0xF, 0xF, true));
+        P[j] = P[j] * sg + p;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j > 0) {
+            const float t = sh * (float)(int)P[j].x;
+            x[j] = __builtin_fmaf(t, kInvSqrt32Hi, t * kInvSqrt32Lo);
+        }
+        const float t2 = sh * (float)(int)P[j].y;
+        x[j + 8] = __builtin_fmaf(t2, kInvSqrt32Hi, t2 * kInvSqrt32Lo);
+    }
+    // position 0 of the group (even lane) carries -32 z16
+    const int m0 = (int)P[0].x - (odd ? 0 : 32 * (int)zh);
+    x[0] = (float)(((double)sh * (double)m0) * kInvSqrt32);
+}
+
 __device__ __forceinline__ float pair_minf(float a) {
     const float p = __builtin_bit_cast(
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, true));
@@ -158,6 +239,19 @@ __device__ __forceinline__ float u8_code(float y, const U8Params &p) {
 // Four codes (FP32 integers in [0, 255]) packed little-endian.
 __device__ __forceinline__ uint32_t pack4_u8(float c0, float c1, float c2, float c3) {
     return pack4_codes(c0, c1, c2, c3);
+}
+
+// The codes of four transformed values, packed little-endian: u8_code's
+// round(y / s16) + z16, saturated by v_cvt_pk_u8_f32, which converts to an
+// unsigned byte with saturation to [0, 255] (NaN to 0; its input here is an
+// integer, so its rounding never applies) and writes the byte in place: one
+// instruction in place of the clamp and the packing step.
+__device__ __forceinline__ uint32_t u8_pack4(float y0, float y1, float y2, float y3,
+                                             const U8Params &p) {
+    uint32_t d = __builtin_amdgcn_cvt_pk_u8_f32(rintf(quant_quotient(y0, p.rinv)) + p.zh, 0u, 0u);
+    d = __builtin_amdgcn_cvt_pk_u8_f32(rintf(quant_quotient(y1, p.rinv)) + p.zh, 1u, d);
+    d = __builtin_amdgcn_cvt_pk_u8_f32(rintf(quant_quotient(y2, p.rinv)) + p.zh, 2u, d);
+    return __builtin_amdgcn_cvt_pk_u8_f32(rintf(quant_quotient(y3, p.rinv)) + p.zh, 3u, d);
 }
 
 // Reconstruction in the transformed domain: RN32(s16 * (code - z16)).

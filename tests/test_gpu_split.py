@@ -2,7 +2,9 @@
 whole-unit kernel: both perform the same operations in the same order, so on
 identical stored bytes and operands they must give the same outputs and the
 same stored bytes, bit for bit, at every step.  Both are also checked against
-the oracle in test_gpu_decode.py (exact trajectories and derived bounds)."""
+the oracle in test_gpu_decode.py (exact trajectories and derived bounds).  The
+default mode's mix of the two in one launch (whole units, then a tail of
+half-unit workgroups, on large grids) is checked against each."""
 import numpy as np
 import pytest
 import torch
@@ -78,3 +80,33 @@ def test_halves_equal_whole_unit_full_heads(kind, cfg):
         for t in range(3):
             assert np.array_equal(ow[t].view(np.uint32), oh[t].view(np.uint32)), f"n={n} step {t}"
             assert np.array_equal(sw[t], sh[t]), f"n={n} step {t}: stored bytes differ"
+
+
+@pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
+@pytest.mark.parametrize("io_bf16", [False, True])
+def test_half_unit_tail_equals_whole_unit(kind, cfg, io_bf16):
+    """A grid of more than two generations of resident workgroups (100 slots x
+    32 heads = 3,200 units) in the default mode ends with half-unit
+    workgroups; outputs and stored bytes equal those of whole units only and
+    of halves only, bit for bit, including unknown slot ids inside and
+    outside the tail."""
+    H, n, steps = 32, 100, 3
+    num_slots = n + 3
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    slots = np.random.default_rng(41).permutation(num_slots)[:n].astype(np.int32)
+    slots[3] = -1
+    slots[97] = num_slots + 5
+    S0 = inputs.initial_state(cfg, n, H)
+    steps_in = [inputs.step_inputs(cfg, t, n, H, kind) for t in range(steps)]
+    runs = {m: _run(m, kind, io_bf16, S0, slots, None, steps_in, num_slots, H, perm, c)
+            for m in (binding.DECODE_SPLIT_AUTO, binding.DECODE_SPLIT_WHOLE,
+                      binding.DECODE_SPLIT_HALVES)}
+    oa, sa = runs[binding.DECODE_SPLIT_AUTO]
+    for m in (binding.DECODE_SPLIT_WHOLE, binding.DECODE_SPLIT_HALVES):
+        om, sm = runs[m]
+        for t in range(steps):
+            assert np.array_equal(oa[t].view(np.uint32), om[t].view(np.uint32)), f"mode {m} step {t}"
+            assert np.array_equal(sa[t], sm[t]), f"mode {m} step {t}: stored bytes differ"
+    bad = (slots < 0) | (slots >= num_slots)
+    assert np.all(np.isnan(oa[-1][bad])) and np.all(np.isfinite(oa[-1][~bad]))

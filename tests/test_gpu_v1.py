@@ -97,6 +97,67 @@ def test_exact_trajectory_bit_exact(kind):
         assert_units_equal(split_gpu(gp, slots), oracle_units(op, slots), f"step {t}")
 
 
+def _edge_states(n, H):
+    """Stored-order states whose groups reach the edges of the decode's
+    integer inverse transform: zero points far outside [0, 255] (the group's
+    transformed values all of one sign), on both sides of the range in which
+    that transform is exact, and all-zero groups (s16 = 0).  A group with
+    only positions 0 and 1 nonzero, (a, b), transforms to (a +- b) / sqrt(32),
+    so z16 = -round(127.5 (a / b - 1)) for a > 0."""
+    r = np.random.default_rng(23)
+    S = r.normal(0, 0.5, (n, H, DK, DV)).astype(np.float32)
+
+    def spike(u, row, g, a, b):
+        x = S[u // H, u % H, row]
+        x[32 * g:32 * g + 32] = 0
+        x[32 * g], x[32 * g + 1] = a, b
+
+    spike(0, 18, 1, 1.0, 0.01)            # z16 ~ -12,600: beyond the range (wave 0)
+    spike(1, 19, 0, 1.0, 0.05)            # z16 ~ -2,420: inside (wave 0)
+    S[0, 2, 26, 64:96] = 0                # s16 = 0 (wave 1)
+    spike(3, 17, 2, -1.0, 0.05)           # z16 ~ +2,680 (wave 0)
+    spike(3, 25, 3, 1.0, 0.05)            # z16 ~ -2,420 (wave 1)
+    spike(4, 20, 0, 1.0, 1.0 / 62.96)     # z16 ~ -7,900: inside
+    spike(4, 28, 1, 1.0, 1.0 / 65.31)     # z16 ~ -8,200: beyond (wave 1)
+    spike(5, 21, 2, -1.0, 1.0 / 62.53)    # z16 ~ +8,100: inside
+    spike(5, 30, 3, -1.0, 1.0 / 64.1)     # z16 ~ +8,300: beyond (wave 1)
+    return S
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_decode_edge_groups_bit_exact(kind):
+    """Decode steps from stored groups at the edges of the exact integer
+    inverse transform, and from groups outside it (where a wave takes the
+    FP64 transform), equal the oracle bit for bit."""
+    n, H, num_slots, steps = 2, 3, 3, 8
+    r = np.random.default_rng(180 if kind == "gdn" else 181)
+    perm = inputs.protected_perm(71, H)
+    c = r.choice([0.5, 1.0, 2.0], (H, DV)).astype(np.float32)
+    slots = np.array([2, 0], np.int32)
+    S0 = _edge_states(n, H)
+    gp = binding.StatePool(binding.FMT_U8H16, num_slots, H, perm, c)
+    op = oracle.OracleU8Pool(num_slots, H, perm, c)
+    ds = to_dev(slots, torch.int32)
+    gp.store(ds, to_dev(S0), binding.SPACE_STORED)
+    op.store(slots, S0, binding.SPACE_STORED)
+    gu = split_gpu(gp, slots)
+    assert_units_equal(gu, oracle_units(op, slots), "store")
+    meta = gu[2].view(np.float16).astype(np.float64)     # [unit][row][group][s, z]
+    z, sh = meta[..., 1], meta[..., 0]
+    assert (z < -7936).any() and (z > 8191).any()
+    assert ((z >= -7936) & (z <= -7000)).any() and ((z >= 7000) & (z <= 8191)).any()
+    assert (sh == 0).any()
+    kid = 0 if kind == "gdn" else 1
+    for t in range(steps):
+        d = _exact_inputs(r, n, H, kind)
+        fn = gp.gdn_step if kind == "gdn" else gp.kda_step
+        og = fn(ds, to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), to_dev(d["gate"]),
+                to_dev(d["beta"])).cpu().numpy()
+        oo = op.decode_step(slots, d["q"], d["k"], d["v"], d["gate"], d["beta"], kid)
+        assert np.array_equal(og, oo), f"step {t}: outputs differ"
+        assert_units_equal(split_gpu(gp, slots), oracle_units(op, slots), f"step {t}")
+
+
 def _rrmse(a, b):
     a, b = a.astype(np.float64), b.astype(np.float64)
     return float(np.sqrt(((a - b) ** 2).sum() / (b ** 2).sum()))
