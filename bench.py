@@ -497,7 +497,7 @@ PAGED_UPDATES_PER_STEP = PAGED_ACTIVE * 32
 
 
 def run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=5, warm_s=0.5, streams=1,
-              sorted_slots=False):
+              sorted_slots=False, pair=False):
     """Paged decode, inputs drawn on the device with the workload's recipe
     (heavy-tailed initial states with outlier rows in the FP16 channels,
     smoothing on).  streams=1: both calls of a step on one stream, in order;
@@ -506,8 +506,9 @@ def run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=5, warm_s=0
     two chains overlap).  sorted_slots: each call lists its requests in
     ascending slot order (the same random slot ids; the order of requests in
     a batch is the caller's choice), so the workgroups resident at any time
-    touch nearby parts of the 2.65 GB pool.  Returns the pass_stats dict
-    (seconds per step)."""
+    touch nearby parts of the 2.65 GB pool.  pair: both groups in one
+    qrs_decode_step_pair call per step (one launch).  Returns the pass_stats
+    dict (seconds per step)."""
     cfg, H = 4, 32
     perm = inputs.protected_perm(cfg, H)
     c = inputs.smoothing(cfg, H, True)
@@ -533,6 +534,11 @@ def run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=5, warm_s=0
 
     def launch(t):
         a, b = ins["gdn"][t], ins["kda"][t]
+        if pair:
+            pool.pair_step((dsl["gdn"], a["q"], a["k"], a["v"], a["alpha"], a["beta"]),
+                           (dsl["kda"], b["q"], b["k"], b["v"], b["g"], b["beta"]),
+                           out["gdn"], out["kda"])
+            return
         pool.gdn_step(dsl["gdn"], a["q"], a["k"], a["v"], a["alpha"], a["beta"], out["gdn"])
         if side is None:
             pool.kda_step(dsl["kda"], b["q"], b["k"], b["v"], b["g"], b["beta"], out["kda"])
@@ -926,14 +932,20 @@ def main():
                  "us_per_step_at_70pct_of_peak": PAGED_BYTES_PER_STEP / (0.7 * PEAK_HBM_GBS * 1e9) * 1e6,
                  "finite_outputs": st["ok"]}
         log(f"[bench] paged mixed pool: {per * 1e6:.2f} us/step, {paged['frac_of_peak'] * 100:.1f}% of peak")
-        for key, streams, srt, what in (
-                ("two_streams", 2, False, "the same steps, the KDA request group's calls on a second stream "
-                                          "(one fork and one join per timed pass; each group's steps stay in order)"),
-                ("sorted", 1, True, "the same random slot ids, each call listing its requests in ascending "
-                                    "slot order (a scheduling choice of the caller), one stream"),
-                ("sorted_two_streams", 2, True, "ascending slot order and the KDA calls on a second stream")):
+        for key, streams, srt, pr, what in (
+                ("two_streams", 2, False, False,
+                 "the same steps, the KDA request group's calls on a second stream (one fork and one join "
+                 "per timed pass; each group's steps stay in order)"),
+                ("one_launch", 1, False, True,
+                 "the same steps, both request groups in one qrs_decode_step_pair call per step (one launch)"),
+                ("sorted", 1, True, False,
+                 "the same random slot ids, each call listing its requests in ascending slot order (a "
+                 "scheduling choice of the caller), one stream"),
+                ("sorted_two_streams", 2, True, False,
+                 "ascending slot order and the KDA calls on a second stream"),
+                ("sorted_one_launch", 1, True, True, "ascending slot order, one pair call per step")):
             st2 = run_paged(torch, binding, inputs, steps, warmup, use_graph, reps=reps, warm_s=leg_warm,
-                            streams=streams, sorted_slots=srt)
+                            streams=streams, sorted_slots=srt, pair=pr)
             per2 = st2["per_step"]
             paged[key] = {
                 "workload": what,

@@ -202,6 +202,30 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
                        const float *gate, const float *beta, void *o, hipStream_t stream);
 
 /*
+ * A GDN decode step and a KDA decode step on disjoint slots of one pool, as
+ * one call: the two request groups of a model with GDN and KDA layers, or of a
+ * pool whose slots serve both kinds (one packed cache per request slot, DAMP
+ * arXiv HTML, Appendix A.5 "Persistent representation"; the updates of
+ * section 3.1 Eq.(1) and the v2 notes' Eqs.(5)-(6), as in
+ * qrs_gdn_decode_step and qrs_kda_decode_step).  The results, outputs and
+ * stored bytes, are those of qrs_gdn_decode_step(pool, slots_gdn, n_gdn, ...)
+ * followed by qrs_kda_decode_step(pool, slots_kda, n_kda, ...) on the same
+ * stream; on a QRS_FMT_I8F16 pool the two run in one kernel launch, which pays
+ * the launch's ramp and drain once (small grids and the other formats make
+ * the two calls).  Arguments of each group as for those calls (FP32, all
+ * heads); a group with n = 0 may pass NULL pointers.  A slot id in both groups
+ * is undefined behaviour (the two updates of its units would race).
+ * QRS_EINVAL: a NULL pool, a negative n, a NULL pointer of a non-empty group,
+ * or (n_gdn + n_kda) * num_heads beyond 2^31 - 1.  Nothing is enqueued on an
+ * error return.
+ */
+int qrs_decode_step_pair(qrs_pool pool, const int32_t *slots_gdn, int n_gdn, const float *q_gdn,
+                         const float *k_gdn, const float *v_gdn, const float *alpha,
+                         const float *beta_gdn, float *o_gdn, const int32_t *slots_kda, int n_kda,
+                         const float *q_kda, const float *k_kda, const float *v_kda, const float *g,
+                         const float *beta_kda, float *o_kda, hipStream_t stream);
+
+/*
  * Per-window quantization ("LeapQuant: Efficient Linear Attention with
  * Accurate Recurrent State Quantization", section 3.2, Figure 2; buffer size
  * of section 4.3) on a QRS_FMT_I8F16 pool.  The stored state of a slot stays

@@ -33,7 +33,8 @@ HI_OFFSET, LO_OFFSET, SCALE_OFFSET = 0, 4096, 18432
 EXPORTED = (
     "qrs_state_pool_bytes", "qrs_create_state_pool", "qrs_destroy_state_pool", "qrs_pool_info",
     "qrs_store_state", "qrs_dequant_state", "qrs_gdn_decode_step", "qrs_kda_decode_step",
-    "qrs_decode_step_ex", "qrs_window_buffer_bytes", "qrs_window_decode_step",
+    "qrs_decode_step_ex", "qrs_decode_step_pair", "qrs_window_buffer_bytes",
+    "qrs_window_decode_step",
     "qrs_chunked_prefill", "qrs_channel_error", "qrs_persistence_window",
     "qrs_persistence_geometric", "qrs_channel_scores", "qrs_select_protected_channels",
     "qrs_set_decode_split", "qrs_status_string",
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.qrs_set_decode_split.restype = i
     lib.qrs_decode_step_ex.argtypes = [p, i, i, p, i, i, i, p, p, p, p, p, p, p]
     lib.qrs_decode_step_ex.restype = i
+    lib.qrs_decode_step_pair.argtypes = [p, p, i] + [p] * 6 + [p, i] + [p] * 6 + [p]
+    lib.qrs_decode_step_pair.restype = i
     lib.qrs_window_buffer_bytes.argtypes = [i, i, i, i]
     lib.qrs_window_buffer_bytes.restype = sz
     lib.qrs_window_decode_step.argtypes = [p, i, i, p, sz, p, p, i, p, p, p, p, p, p, p]
@@ -291,6 +294,34 @@ class StatePool:
         n = slots.numel()
         return self._step(load().qrs_kda_decode_step, "qrs_kda_decode_step", slots, q, k, v, g,
                           (n, self.num_heads, DK), beta, out)
+
+    def pair_step(self, gdn, kda, out_gdn=None, out_kda=None):
+        """qrs_decode_step_pair: a GDN step and a KDA step on disjoint slots
+        in one call.  gdn = (slots, q, k, v, alpha, beta), kda = (slots, q, k,
+        v, g, beta), float32 [n][H][128] operands as for gdn_step / kda_step.
+        Returns (o_gdn, o_kda)."""
+        H = self.num_heads
+        args, outs = [], []
+        for grp, out, gshape_of, name in ((gdn, out_gdn, lambda n: (n, H), "gdn"),
+                                          (kda, out_kda, lambda n: (n, H, DK), "kda")):
+            slots, q, k, v, gate, beta = grp
+            n = slots.numel()
+            if out is None:
+                out = torch.empty((n, H, DV), dtype=torch.float32, device=self.mem.device)
+            if n == 0:
+                args += [None, 0] + [None] * 6
+            else:
+                args += [_dev(slots, torch.int32, (n,), f"{name} slots"), n,
+                         _dev(q, torch.float32, (n, H, DK), f"{name} q"),
+                         _dev(k, torch.float32, (n, H, DK), f"{name} k"),
+                         _dev(v, torch.float32, (n, H, DV), f"{name} v"),
+                         _dev(gate, torch.float32, gshape_of(n), f"{name} gate"),
+                         _dev(beta, torch.float32, (n, H), f"{name} beta"),
+                         _dev(out, torch.float32, (n, H, DV), f"{name} o")]
+            outs.append(out)
+        st = load().qrs_decode_step_pair(self.handle, *args, _stream())
+        _check(st, "qrs_decode_step_pair")
+        return outs[0], outs[1]
 
 
 def split_units(raw: np.ndarray):

@@ -22,6 +22,12 @@ hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &poo
                                 const int32_t *slots, int n, int h0, int hc, const void *q,
                                 const void *k, const void *v, const float *gate, const float *beta,
                                 void *o, bool half_tail, hipStream_t stream);
+hipError_t launch_decode_pair(const PoolView &pool, const int32_t *slots_g, int n_g,
+                              const float *q_g, const float *k_g, const float *v_g,
+                              const float *alpha, const float *beta_g, float *o_g,
+                              const int32_t *slots_k, int n_k, const float *q_k, const float *k_k,
+                              const float *v_k, const float *g, const float *beta_k, float *o_k,
+                              bool half_tail, hipStream_t stream);
 hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n, int h0,
                              int hc, const float *q, const float *k, const float *v,
                              const float *gate, const float *beta, float *o, hipStream_t stream);
@@ -282,6 +288,40 @@ int qrs_kda_decode_step(qrs_pool pool, const int32_t *slots, int n, const float 
                         float *o, hipStream_t stream) {
     return decode_common(1, 0, pool, slots, n, 0, pool ? pool->num_heads : 1, q, k, v, g, beta, o,
                          stream);
+}
+
+int qrs_decode_step_pair(qrs_pool pool, const int32_t *slots_gdn, int n_gdn, const float *q_gdn,
+                         const float *k_gdn, const float *v_gdn, const float *alpha,
+                         const float *beta_gdn, float *o_gdn, const int32_t *slots_kda, int n_kda,
+                         const float *q_kda, const float *k_kda, const float *v_kda, const float *g,
+                         const float *beta_kda, float *o_kda, hipStream_t stream) {
+    if (!pool || n_gdn < 0 || n_kda < 0) return QRS_EINVAL;
+    if (n_gdn > 0 && (!slots_gdn || !q_gdn || !k_gdn || !v_gdn || !alpha || !beta_gdn || !o_gdn))
+        return QRS_EINVAL;
+    if (n_kda > 0 && (!slots_kda || !q_kda || !k_kda || !v_kda || !g || !beta_kda || !o_kda))
+        return QRS_EINVAL;
+    if (((size_t)n_gdn + (size_t)n_kda) * (size_t)pool->num_heads > 0x7fffffffu) return QRS_EINVAL;
+    const int units = (n_gdn + n_kda) * pool->num_heads;
+    const int mode = g_decode_split.load(std::memory_order_relaxed);
+    if (pool->fmt != QRS_FMT_I8F16 || n_gdn == 0 || n_kda == 0 ||
+        mode == QRS_DECODE_SPLIT_HALVES ||
+        (mode == QRS_DECODE_SPLIT_AUTO && units < kDecodeSplitUnits)) {
+        // the two calls, as a caller would make them (every argument is valid
+        // by the checks above, so neither returns an argument error)
+        const int st = decode_common(0, 0, pool, slots_gdn, n_gdn, 0, pool->num_heads, q_gdn, k_gdn,
+                                     v_gdn, alpha, beta_gdn, o_gdn, stream);
+        if (st != QRS_OK) return st;
+        return decode_common(1, 0, pool, slots_kda, n_kda, 0, pool->num_heads, q_kda, k_kda, v_kda,
+                             g, beta_kda, o_kda, stream);
+    }
+    DeviceGuard dg(pool->device);
+    if (!dg.ok) return QRS_EDEVICE;
+    return qrs::launch_decode_pair(view(pool), slots_gdn, n_gdn, q_gdn, k_gdn, v_gdn, alpha,
+                                   beta_gdn, o_gdn, slots_kda, n_kda, q_kda, k_kda, v_kda, g,
+                                   beta_kda, o_kda, mode == QRS_DECODE_SPLIT_AUTO,
+                                   stream) == hipSuccess
+               ? QRS_OK
+               : QRS_EDEVICE;
 }
 
 int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slots, int n,

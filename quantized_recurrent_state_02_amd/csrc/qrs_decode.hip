@@ -48,39 +48,41 @@ namespace qrs {
 // INT8 tier may end its grid with half-unit workgroups (i >= nwhole, two per
 // unit, qrs_decode_half.h) for units nwhole .. units - 1: they live about
 // half as long, so the launch drains sooner (the launcher below).
-// The INT8 tier is held to 168 VGPRs, three waves per SIMD (six units per
-// CU); at 180 VGPRs it ran two waves per SIMD and was 3-4% slower.  The
-// first revision's tier needs about 200 VGPRs for its transforms and stays
-// at two waves per SIMD.
 template <int CODEC>
 struct DecodeOccupancy {
     static constexpr int waves = CODEC == 0 ? 3 : 2;
 };
 
-template <int KIND, int CODEC, int IO>
-__global__ __launch_bounds__(THREADS) __attribute__((
-    amdgpu_waves_per_eu(DecodeOccupancy<CODEC>::waves, DecodeOccupancy<CODEC>::waves))) void
-decode_packed_kernel(
-    PoolView pool, const int32_t *__restrict__ slots, int first_gen, int n_cus, int h0, int hc,
-    int nwhole, int units, const void *__restrict__ q, const void *__restrict__ k,
-    const void *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta, void *__restrict__ o) {
-    __shared__ float s_k[DK];
-    __shared__ float s_q[DK];
-    __shared__ float s_dec[DK];
-    __shared__ float s_bd[DV];
-    __shared__ float s_vp[DV];
-    __shared__ float s_kraw[DK];
-    __shared__ float s_qraw[DK];
-    __shared__ float s_graw[DK];
-    __shared__ float s_qk[2];
-    __shared__ float4 red_w[16][DV / 4];
-    __shared__ float4 red_z[16][DV / 4];
+// LDS of a whole-unit workgroup (the kernel's own arrays, lent to the body).
+struct DecodeLds {
+    float *s_k, *s_q, *s_dec;          // [DK]
+    float *s_bd, *s_vp;                // [DV]
+    float *s_kraw, *s_qraw, *s_graw;   // [DK]
+    float *s_qk;                       // [2]
+    float4 (*red_w)[DV / 4];           // [16][DV / 4]
+    float4 (*red_z)[DV / 4];
+};
 
-    if (CODEC == 0 && (int)blockIdx.x >= nwhole) {
-        const HalfLds L{s_k,    s_q,    s_dec, s_bd,         s_vp,        s_kraw,
-                        s_qraw, s_graw, s_qk,  &red_w[0][0], &red_z[0][0]};
-        decode_half_unit<KIND, IO>(pool, slots, units, h0, hc, (int)blockIdx.x - nwhole, nwhole, q,
-                                   k, v, gate, beta, o, L);
+// One workgroup's share of a decode call: workgroup bid < nwhole owns unit
+// bid, a later one half of a unit of the half-unit tail.
+template <int KIND, int CODEC, int IO>
+__device__ __forceinline__ void decode_unit(
+    PoolView pool, const int32_t *__restrict__ slots, int bid, int first_gen, int n_cus, int h0,
+    int hc, int nwhole, int units, const void *__restrict__ q, const void *__restrict__ k,
+    const void *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta,
+    void *__restrict__ o, const DecodeLds &L) {
+    float *const s_k = L.s_k, *const s_q = L.s_q, *const s_dec = L.s_dec;
+    float *const s_bd = L.s_bd, *const s_vp = L.s_vp;
+    float *const s_kraw = L.s_kraw, *const s_qraw = L.s_qraw, *const s_graw = L.s_graw;
+    float *const s_qk = L.s_qk;
+    float4 (*const red_w)[DV / 4] = L.red_w;
+    float4 (*const red_z)[DV / 4] = L.red_z;
+
+    if (CODEC == 0 && bid >= nwhole) {
+        const HalfLds HL{s_k,    s_q,    s_dec, s_bd,         s_vp,        s_kraw,
+                         s_qraw, s_graw, s_qk,  &red_w[0][0], &red_z[0][0]};
+        decode_half_unit<KIND, IO>(pool, slots, units, h0, hc, bid - nwhole, nwhole, q, k, v, gate,
+                                   beta, o, HL);
         return;
     }
     // Staggered start of the first generation (the workgroups resident at
@@ -88,8 +90,8 @@ decode_packed_kernel(
     // workgroup placed on each CU waits j x 2048 cycles (~0.85 us), so the
     // first workgroups get their state sooner and compute while the others
     // load, instead of all loading and then all computing at once.
-    if ((int)blockIdx.x < first_gen) {
-        const int j = (int)blockIdx.x / n_cus;
+    if (bid < first_gen) {
+        const int j = bid / n_cus;
         for (int i = 0; i < j; ++i) __builtin_amdgcn_s_sleep(32);
     }
     // Raised wave priority until the state loads are issued: a workgroup
@@ -99,8 +101,9 @@ decode_packed_kernel(
     __builtin_amdgcn_s_setprio(3);
     const int tid = threadIdx.x;
     const int H = pool.num_heads;
-    const int b = blockIdx.x / hc;
-    const int h = h0 + (blockIdx.x - b * hc);
+    const unsigned ubid = (unsigned)bid;
+    const int b = ubid / hc;
+    const int h = h0 + (ubid - b * hc);
     const int uu = b * H + h;
     const int slot = slots[b];
     if (slot < 0 || slot >= pool.num_slots) {
@@ -343,14 +346,81 @@ decode_packed_kernel(
     }
 }
 
+// The INT8 tier is held to 168 VGPRs, three waves per SIMD (six units per
+// CU); at 180 VGPRs it ran two waves per SIMD and was 3-4% slower.  The
+// first revision's tier needs about 200 VGPRs for its transforms and stays
+// at two waves per SIMD.
+template <int KIND, int CODEC, int IO>
+__global__ __launch_bounds__(THREADS) __attribute__((
+    amdgpu_waves_per_eu(DecodeOccupancy<CODEC>::waves, DecodeOccupancy<CODEC>::waves))) void
+decode_packed_kernel(PoolView pool, const int32_t *__restrict__ slots, int first_gen, int n_cus,
+                     int h0, int hc, int nwhole, int units, const void *__restrict__ q,
+                     const void *__restrict__ k, const void *__restrict__ v,
+                     const float *__restrict__ gate, const float *__restrict__ beta,
+                     void *__restrict__ o) {
+    __shared__ float s_k[DK];
+    __shared__ float s_q[DK];
+    __shared__ float s_dec[DK];
+    __shared__ float s_bd[DV];
+    __shared__ float s_vp[DV];
+    __shared__ float s_kraw[DK];
+    __shared__ float s_qraw[DK];
+    __shared__ float s_graw[DK];
+    __shared__ float s_qk[2];
+    __shared__ float4 red_w[16][DV / 4];
+    __shared__ float4 red_z[16][DV / 4];
+    const DecodeLds L{s_k, s_q, s_dec, s_bd, s_vp, s_kraw, s_qraw, s_graw, s_qk, red_w, red_z};
+    decode_unit<KIND, CODEC, IO>(pool, slots, (int)blockIdx.x, first_gen, n_cus, h0, hc, nwhole,
+                                 units, q, k, v, gate, beta, o, L);
+}
+
+
+// One launch for a GDN call and a KDA call on disjoint slots of one INT8-tier
+// pool, all heads, FP32 operands: the two request groups of a model with GDN
+// and KDA layers, or of a pool shared by such models.  Workgroups [0, ug) run
+// the GDN units in the order of the GDN call, the rest the KDA units in the
+// order of the KDA call (with their half-unit tail at the end of the grid), so
+// the pair pays the launch ramp and drain once.  Each unit's arithmetic is
+// that of decode_packed_kernel, so the results are those of the two calls.
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void
+decode_pair_kernel(PoolView pool, int first_gen, int n_cus, int ug, int uk, int nwhole_k,
+                   const int32_t *__restrict__ slots_g, const float *__restrict__ q_g,
+                   const float *__restrict__ k_g, const float *__restrict__ v_g,
+                   const float *__restrict__ alpha, const float *__restrict__ beta_g,
+                   float *__restrict__ o_g, const int32_t *__restrict__ slots_k,
+                   const float *__restrict__ q_k, const float *__restrict__ k_k,
+                   const float *__restrict__ v_k, const float *__restrict__ g,
+                   const float *__restrict__ beta_k, float *__restrict__ o_k) {
+    __shared__ float s_k[DK];
+    __shared__ float s_q[DK];
+    __shared__ float s_dec[DK];
+    __shared__ float s_bd[DV];
+    __shared__ float s_vp[DV];
+    __shared__ float s_kraw[DK];
+    __shared__ float s_qraw[DK];
+    __shared__ float s_graw[DK];
+    __shared__ float s_qk[2];
+    __shared__ float4 red_w[16][DV / 4];
+    __shared__ float4 red_z[16][DV / 4];
+    const DecodeLds L{s_k, s_q, s_dec, s_bd, s_vp, s_kraw, s_qraw, s_graw, s_qk, red_w, red_z};
+    const int H = pool.num_heads;
+    const int i = (int)blockIdx.x;
+    if (i < ug)
+        decode_unit<0, 0, 0>(pool, slots_g, i, first_gen, n_cus, 0, H, ug, ug, q_g, k_g, v_g, alpha,
+                             beta_g, o_g, L);
+    else
+        decode_unit<1, 0, 0>(pool, slots_k, i - ug, 0, n_cus, 0, H, nwhole_k, uk, q_k, k_k, v_k, g,
+                             beta_k, o_k, L);
+}
+
 // Launcher (host): one workgroup per (slot, head) unit of heads [h0, h0 + hc).
 // The number of workgroups resident at launch (occupancy x CUs) is queried
 // once per device and kernel.
 // The cache is per device; host threads launching concurrently may both
 // query it first, which is harmless (they store the same values).
-template <int K, int C, int I>
-static void decode_residency(int *per_cu, int *cus) {
-    static std::atomic<int> s_per[16], s_cus[16];
+template <typename Kernel>
+static void residency(Kernel kernel, std::atomic<int> (&s_per)[16], std::atomic<int> (&s_cus)[16],
+                      int *per_cu, int *cus) {
     int dev = 0;
     *per_cu = 0;
     *cus = 1;
@@ -358,8 +428,7 @@ static void decode_residency(int *per_cu, int *cus) {
     int p = s_per[dev].load(std::memory_order_acquire);
     int c = s_cus[dev].load(std::memory_order_relaxed);
     if (p == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, decode_packed_kernel<K, C, I>, THREADS,
-                                                         0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, kernel, THREADS, 0) != hipSuccess ||
             hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             c <= 0 || p <= 0)
             return;
@@ -368,6 +437,11 @@ static void decode_residency(int *per_cu, int *cus) {
     }
     *per_cu = p;
     *cus = c;
+}
+template <int K, int C, int I>
+static void decode_residency(int *per_cu, int *cus) {
+    static std::atomic<int> s_per[16], s_cus[16];
+    residency(decode_packed_kernel<K, C, I>, s_per, s_cus, per_cu, cus);
 }
 // The stagger pays off only when later generations follow the first, and so
 // does the half-unit tail: when the grid holds more than two generations of
@@ -405,5 +479,31 @@ hipError_t launch_decode_packed(int kind, int codec, int io, const PoolView &poo
     return hipErrorInvalidValue;
 }
 #undef QRS_DECODE_CASE
+
+// The pair launch: the stagger on the first generation (GDN units first), the
+// half-unit tail on the KDA units at the end of the grid, with the same rules
+// as a single call over ug + uk units.
+hipError_t launch_decode_pair(const PoolView &pool, const int32_t *slots_g, int n_g,
+                              const float *q_g, const float *k_g, const float *v_g,
+                              const float *alpha, const float *beta_g, float *o_g,
+                              const int32_t *slots_k, int n_k, const float *q_k, const float *k_k,
+                              const float *v_k, const float *g, const float *beta_k, float *o_k,
+                              bool half_tail, hipStream_t stream) {
+    static std::atomic<int> s_per[16], s_cus[16];
+    int per_cu = 0, cus = 1;
+    residency(decode_pair_kernel, s_per, s_cus, &per_cu, &cus);
+    const int H = pool.num_heads;
+    const int ug = n_g * H, uk = n_k * H, resident = per_cu * cus;
+    const bool big = ug + uk > 2 * resident;
+    const int first_gen = big ? resident : 0;
+    int tail = half_tail && big ? (resident / 8) & ~7 : 0;
+    if (tail > uk / 2) tail = 0;
+    const int nwhole_k = uk - tail;
+    dim3 grid((unsigned)(ug + nwhole_k + 16 * ((tail + 7) / 8))), block(THREADS);
+    hipLaunchKernelGGL(decode_pair_kernel, grid, block, 0, stream, pool, first_gen, cus, ug, uk,
+                       nwhole_k, slots_g, q_g, k_g, v_g, alpha, beta_g, o_g, slots_k, q_k, k_k,
+                       v_k, g, beta_k, o_k);
+    return hipGetLastError();
+}
 
 }  // namespace qrs

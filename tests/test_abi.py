@@ -163,6 +163,13 @@ def test_decode_step_ex_rejects_null_pool(lib):
     assert lib.qrs_decode_step_ex(None, 0, 0, p, 1, 0, 1, p, p, p, p, p, p, None) == -1
 
 
+def test_decode_step_pair_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(0x10000)
+    grp = [p] * 6
+    assert lib.qrs_decode_step_pair(None, p, 1, *grp, p, 1, *grp, None) == -1
+    assert lib.qrs_decode_step_pair(None, None, 0, *([None] * 6), None, 0, *([None] * 6), None) == -1
+
+
 def test_window_buffer_bytes_and_null_pool(lib):
     f = lib.qrs_window_buffer_bytes
     assert f(0, 4, 32, 16) == 4 * 32 * 16 * 528      # GDN record: k, v FP16 + beta, alpha

@@ -1,0 +1,82 @@
+"""qrs_decode_step_pair (a GDN step and a KDA step on disjoint slots of one
+pool in one call) against the two separate calls, qrs_gdn_decode_step then
+qrs_kda_decode_step, which the decode tests check against the oracle: outputs
+and stored bytes equal bit for bit at every step.  Cases: a grid large enough
+for the one-launch kernel with its half-unit tail (and without the tail, whole
+units only), a small grid (the two calls), an empty group, and unknown slot
+ids in both groups."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_recurrent_state_02_amd import binding, inputs
+from tests.parity_util import to_dev
+
+pytestmark = pytest.mark.gpu
+DK = DV = 128
+
+
+def _setup(H, n_g, n_k, num_slots, seed):
+    perm = inputs.protected_perm(1, H)
+    c = inputs.smoothing(1, H, True)
+    ids = np.random.default_rng(seed).permutation(num_slots).astype(np.int32)
+    sg, sk = ids[:n_g].copy(), ids[n_g:n_g + n_k].copy()
+    S = inputs.initial_state(1, n_g + n_k, H)
+    pools = []
+    for _ in range(2):
+        gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+        gp.units().zero_()
+        gp.store(to_dev(ids[:n_g + n_k], torch.int32), to_dev(S))
+        pools.append(gp)
+    return pools, sg, sk
+
+
+def _steps(H, n_g, n_k, steps, seed):
+    out = []
+    for t in range(steps):
+        dg = inputs.step_inputs(1, seed + t, max(n_g, 1), H, "gdn")
+        dk = inputs.step_inputs(2, seed + t, max(n_k, 1), H, "kda")
+        dk["g"][0, 0, :7] = -np.inf                       # zero decays on some channels
+        out.append(({key: val[:n_g] for key, val in dg.items()},
+                    {key: val[:n_k] for key, val in dk.items()}))
+    return out
+
+
+def _run_both(H, n_g, n_k, num_slots, steps, seed, bad_g=None, bad_k=None):
+    (pa, pb), sg, sk = _setup(H, n_g, n_k, num_slots, seed)
+    if bad_g is not None and n_g:
+        sg[bad_g] = -1
+    if bad_k is not None and n_k:
+        sk[bad_k] = num_slots + 7
+    dsg, dsk = to_dev(sg, torch.int32), to_dev(sk, torch.int32)
+    for t, (dg, dk) in enumerate(_steps(H, n_g, n_k, steps, seed)):
+        g_args = (dsg, to_dev(dg["q"]), to_dev(dg["k"]), to_dev(dg["v"]), to_dev(dg["alpha"]),
+                  to_dev(dg["beta"]))
+        k_args = (dsk, to_dev(dk["q"]), to_dev(dk["k"]), to_dev(dk["v"]), to_dev(dk["g"]),
+                  to_dev(dk["beta"]))
+        og_a, ok_a = pa.pair_step(g_args, k_args)
+        og_b = pb.gdn_step(*g_args) if n_g else torch.empty((0, H, DV), device="cuda")
+        ok_b = pb.kda_step(*k_args) if n_k else torch.empty((0, H, DV), device="cuda")
+        for a, b, nm in ((og_a, og_b, "gdn"), (ok_a, ok_b, "kda")):
+            a, b = a.cpu().numpy(), b.cpu().numpy()
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"step {t}: {nm} outputs differ"
+        assert torch.equal(pa.units(), pb.units()), f"step {t}: stored bytes differ"
+    return og_a.cpu().numpy(), ok_a.cpu().numpy(), sg, sk
+
+
+@pytest.mark.parametrize("mode", [binding.DECODE_SPLIT_AUTO, binding.DECODE_SPLIT_WHOLE])
+def test_pair_one_launch_equals_two_calls(mode):
+    """60 GDN + 60 KDA requests x 32 heads = 3,840 units: the one-launch
+    kernel, with the half-unit tail on the KDA units in the default mode."""
+    prev = binding.set_decode_split(mode)
+    try:
+        og, ok, sg, sk = _run_both(32, 60, 60, 131, 3, 5, bad_g=17, bad_k=59)
+    finally:
+        binding.set_decode_split(prev)
+    assert np.all(np.isnan(og[17])) and np.all(np.isfinite(np.delete(og, 17, axis=0)))
+    assert np.all(np.isnan(ok[59])) and np.all(np.isfinite(ok[:59]))
+
+
+@pytest.mark.parametrize("n_g,n_k", [(3, 2), (0, 5), (4, 0)])
+def test_pair_small_and_empty_groups(n_g, n_k):
+    _run_both(4, n_g, n_k, 11, 2, 9)
