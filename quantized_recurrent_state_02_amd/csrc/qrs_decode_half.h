@@ -150,13 +150,18 @@ __device__ __forceinline__ void decode_half_unit(
         sc_old[r - 1] = buf_loadf(st, off_sc + 256 * (r - 1), SC_OFF);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // v is used by the first 64 threads only; this keeps its load where it
+    // is, ahead of the state loads, instead of inside that branch behind them
+    // (where its wait was a wait for every state load)
+    float v_keep = v_m;
+    asm volatile("" : "+v"(v_keep));
 
     // ---- gather through pi ----
     const float beta_u = beta[uu];
     s_kraw[tid] = k_m;
     s_qraw[tid] = q_m;
     if (KIND == 1) s_graw[tid] = g_m;
-    if (tid < HCOLS) s_vp[tid] = v_m / c_t;
+    if (tid < HCOLS) s_vp[tid] = v_keep / c_t;
     __syncthreads();
     const float kt = s_kraw[src];
     const float qt = s_qraw[src];
