@@ -370,9 +370,9 @@ int qrs_select_protected_channels(int num_heads, const double *score_host, int k
  *     fill the GPU (a whole-unit workgroup's lifetime then sets the step);
  *   QRS_DECODE_SPLIT_AUTO (the default): the halves below 1,024 units per call
  *     (n * head count), where on MI355X they are faster; above, whole units,
- *     and for grids of more than two generations of resident workgroups the
- *     last eighth of a generation's units as halves, at the end of the same
- *     launch, which shortens its drain.
+ *     and for grids of at least 4/3 of a generation of resident workgroups
+ *     the last eighth of a generation's units as halves, at the end of the
+ *     same launch, which shortens its drain.
  * The setting is process-wide, applies to calls enqueued after it returns,
  * and is a tuning choice only.  Returns the previous mode (>= 0), or
  * QRS_EINVAL for another value (the setting is then unchanged).  Other pool

@@ -128,7 +128,10 @@ struct DeviceGuard {
 // (value-column halves) for grids too small to fill the GPU.
 // QRS_DECODE_SPLIT_AUTO picks the halves below kDecodeSplitUnits units, and
 // above lets the whole-unit kernel end a large grid with half-unit
-// workgroups; QRS_DECODE_SPLIT_WHOLE uses whole-unit workgroups only.
+// workgroups; QRS_DECODE_SPLIT_WHOLE uses whole-unit workgroups only.  At
+// exactly 1,024 units the better kernel depends on the layout on MI355X:
+// halves 11.25 against 11.55 us for 32 slots x 32 heads, but 11.66 against
+// 10.87 for 256 slots x 4 heads (scattered units), so whole units stay there.
 std::atomic<int> g_decode_split{QRS_DECODE_SPLIT_AUTO};
 constexpr int kDecodeSplitUnits = 1024;
 

@@ -443,13 +443,15 @@ static void decode_residency(int *per_cu, int *cus) {
     static std::atomic<int> s_per[16], s_cus[16];
     residency(decode_packed_kernel<K, C, I>, s_per, s_cus, per_cu, cus);
 }
-// The stagger pays off only when later generations follow the first, and so
-// does the half-unit tail: when the grid holds more than two generations of
-// resident workgroups (INT8 tier, half_tail set), the last resident / 8 units
-// (a multiple of 8) run as value-column halves.  On MI355X at batch 256 x 32
-// heads (6 x 256 resident) this took 0.5-0.7 us off a 60.5 us step for GDN and
+// The stagger pays off only when the grid holds more than two generations of
+// resident workgroups.  The half-unit tail (INT8 tier, half_tail set): when
+// the grid holds at least 4/3 of a generation, its last resident / 8 units (a
+// multiple of 8) run as value-column halves.  On MI355X (6 x 256 resident)
+// this took 0.5-0.7 us off a 60.5 us step at batch 256 x 32 heads for GDN and
 // KDA on two boxes (tails of 192, 256 and 384 units within noise of each
-// other; 512 gained less, 1,536 lost 1.5 us).
+// other; 512 gained less, 1,536 lost 1.5 us), 1.4 us off 21.5 at batch 64 and
+// off 27.7 at batch 96; at batch 56 (1,792 units) it cost 0.2 us and at
+// exactly one generation (batch 48) 1.0 us.
 #define QRS_DECODE_CASE(K, C, I)                                                                  \
     if (kind == K && codec == C && io == I) {                                                     \
         int per_cu = 0, cus = 1;                                                                  \
@@ -457,7 +459,9 @@ static void decode_residency(int *per_cu, int *cus) {
         const int units = n * hc, resident = per_cu * cus;                                        \
         const bool big = units > 2 * resident;                                                    \
         const int first_gen = big ? resident : 0;                                                 \
-        const int tail = C == 0 && half_tail && big ? (resident / 8) & ~7 : 0;                    \
+        const bool tailed =                                                                       \
+            C == 0 && half_tail && 3 * (int64_t)units >= 4 * (int64_t)resident;                   \
+        const int tail = tailed ? (resident / 8) & ~7 : 0;                                        \
         const int nwhole = units - tail;                                                          \
         dim3 grid((unsigned)(nwhole + 16 * ((tail + 7) / 8))), block(THREADS);                    \
         hipLaunchKernelGGL((decode_packed_kernel<K, C, I>), grid, block, 0, stream, pool, slots,  \
@@ -496,7 +500,8 @@ hipError_t launch_decode_pair(const PoolView &pool, const int32_t *slots_g, int 
     const int ug = n_g * H, uk = n_k * H, resident = per_cu * cus;
     const bool big = ug + uk > 2 * resident;
     const int first_gen = big ? resident : 0;
-    int tail = half_tail && big ? (resident / 8) & ~7 : 0;
+    const bool tailed = half_tail && 3 * ((int64_t)ug + uk) >= 4 * (int64_t)resident;
+    int tail = tailed ? (resident / 8) & ~7 : 0;
     if (tail > uk / 2) tail = 0;
     const int nwhole_k = uk - tail;
     dim3 grid((unsigned)(ug + nwhole_k + 16 * ((tail + 7) / 8))), block(THREADS);

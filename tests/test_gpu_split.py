@@ -84,19 +84,20 @@ def test_halves_equal_whole_unit_full_heads(kind, cfg):
 
 @pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
 @pytest.mark.parametrize("io_bf16", [False, True])
-def test_half_unit_tail_equals_whole_unit(kind, cfg, io_bf16):
-    """A grid of more than two generations of resident workgroups (100 slots x
-    32 heads = 3,200 units) in the default mode ends with half-unit
-    workgroups; outputs and stored bytes equal those of whole units only and
-    of halves only, bit for bit, including unknown slot ids inside and
-    outside the tail."""
-    H, n, steps = 32, 100, 3
+@pytest.mark.parametrize("n", [100, 65])
+def test_half_unit_tail_equals_whole_unit(kind, cfg, io_bf16, n):
+    """Grids of at least 4/3 of a generation of resident workgroups (100 or
+    65 slots x 32 heads = 3,200 or 2,080 units, against 1,536 resident on
+    MI355X) in the default mode end with half-unit workgroups; outputs and
+    stored bytes equal those of whole units only and of halves only, bit for
+    bit, including unknown slot ids inside and outside the tail."""
+    H, steps = 32, 3
     num_slots = n + 3
     perm = inputs.protected_perm(cfg, H)
     c = inputs.smoothing(cfg, H, True)
     slots = np.random.default_rng(41).permutation(num_slots)[:n].astype(np.int32)
     slots[3] = -1
-    slots[97] = num_slots + 5
+    slots[n - 3] = num_slots + 5
     S0 = inputs.initial_state(cfg, n, H)
     steps_in = [inputs.step_inputs(cfg, t, n, H, kind) for t in range(steps)]
     runs = {m: _run(m, kind, io_bf16, S0, slots, None, steps_in, num_slots, H, perm, c)
