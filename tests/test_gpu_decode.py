@@ -178,10 +178,12 @@ def test_reduced_serving_shape(kind, cfg, split):
 @pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
 def test_full_serving_shape_sampled(kind, cfg):
     """256 slots x 32 heads for all 256 steps in the benchmarked launch
-    configuration; the oracle follows 2 seeded slots (64 units) through every
-    step."""
+    configuration; the oracle follows 2 seeded slots and the last slot (96
+    units) through every step.  The last slot's units are among those the
+    launch runs as half-unit workgroups at the end of its grid."""
     wl = inputs.WORKLOADS[cfg]
-    sample = np.sort(np.random.default_rng(cfg).choice(wl.n, 2, replace=False))
+    sample = np.random.default_rng(cfg).choice(wl.n - 1, 2, replace=False)
+    sample = np.sort(np.append(sample, wl.n - 1))
     stats = run_parity(cfg, kind, wl.n, wl.heads, wl.steps, sample, smooth=True)
     print(stats)
 
