@@ -16,15 +16,15 @@ pytestmark = pytest.mark.gpu
 DK = DV = 128
 
 
-def _setup(H, n_g, n_k, num_slots, seed):
-    perm = inputs.protected_perm(1, H)
-    c = inputs.smoothing(1, H, True)
+def _setup(H, n_g, n_k, num_slots, seed, fmt=binding.FMT_I8F16):
+    perm = None if fmt == binding.FMT_FP32 else inputs.protected_perm(1, H)
+    c = None if fmt == binding.FMT_FP32 else inputs.smoothing(1, H, True)
     ids = np.random.default_rng(seed).permutation(num_slots).astype(np.int32)
     sg, sk = ids[:n_g].copy(), ids[n_g:n_g + n_k].copy()
     S = inputs.initial_state(1, n_g + n_k, H)
     pools = []
     for _ in range(2):
-        gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+        gp = binding.StatePool(fmt, num_slots, H, perm, c)
         gp.units().zero_()
         gp.store(to_dev(ids[:n_g + n_k], torch.int32), to_dev(S))
         pools.append(gp)
@@ -42,8 +42,8 @@ def _steps(H, n_g, n_k, steps, seed):
     return out
 
 
-def _run_both(H, n_g, n_k, num_slots, steps, seed, bad_g=None, bad_k=None):
-    (pa, pb), sg, sk = _setup(H, n_g, n_k, num_slots, seed)
+def _run_both(H, n_g, n_k, num_slots, steps, seed, bad_g=None, bad_k=None, fmt=binding.FMT_I8F16):
+    (pa, pb), sg, sk = _setup(H, n_g, n_k, num_slots, seed, fmt)
     if bad_g is not None and n_g:
         sg[bad_g] = -1
     if bad_k is not None and n_k:
@@ -80,3 +80,9 @@ def test_pair_one_launch_equals_two_calls(mode):
 @pytest.mark.parametrize("n_g,n_k", [(3, 2), (0, 5), (4, 0)])
 def test_pair_small_and_empty_groups(n_g, n_k):
     _run_both(4, n_g, n_k, 11, 2, 9)
+
+
+@pytest.mark.parametrize("fmt", [binding.FMT_U8H16, binding.FMT_FP32])
+def test_pair_other_pool_formats(fmt):
+    """On the other pool formats the pair call makes the two calls."""
+    _run_both(4, 3, 2, 9, 2, 13, bad_g=1, fmt=fmt)
