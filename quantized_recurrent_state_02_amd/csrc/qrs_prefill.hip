@@ -649,7 +649,13 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                     *reinterpret_cast<U4 *>(stg + LO_OFF + lr * DV + GRP * gq + 16 * half) =
                         U4{wd[0], wd[1], wd[2], wd[3]};
                     if (!half) reinterpret_cast<uint32_t *>(stg + SC_OFF)[lr * NGRP + gq] = pr.meta;
-                    hadamard32_pair(y, half);
+                    // the reconstruction transformed back: on the integer codes
+                    // when every group of the wave is in the exact range (the
+                    // same bits), else in FP64
+                    if (__builtin_amdgcn_ballot_w64(!u8_group_exact(pr.sh, pr.zh)) == 0)
+                        hadamard32_pair_codes(wd, pr.sh, pr.zh, half != 0, y);
+                    else
+                        hadamard32_pair(y, half);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         *reinterpret_cast<v4f *>(x + 4 * j) =
