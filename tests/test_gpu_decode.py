@@ -78,6 +78,55 @@ def test_exact_trajectory_bit_exact(kind, split):
         assert_units_equal(split_gpu(gp, slots), oracle_units(op, slots), f"step {t}")
 
 
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_degenerate_gates_and_operands_bit_exact(kind, split):
+    """The update's degenerate cases, exact in FP32 so that the GPU and the
+    oracle agree bit for bit: a full decay (alpha = 0, or g = -inf on every
+    channel) that leaves only beta k v^T, beta = 0 (the state only decays),
+    k = 0 (no write), q = 0 (a zero readout), v = 0, a state of zeros, and a
+    state with one huge and one tiny row."""
+    n, H, num_slots, steps = 4, 3, 6, 12
+    r = np.random.default_rng(90 if kind == "gdn" else 91)
+    perm = inputs.protected_perm(72, H)
+    c = r.choice([0.5, 1.0, 2.0], (H, DV)).astype(np.float32)
+    slots = np.array([5, 0, 3, 2], np.int32)
+    S0 = r.normal(0, 1, (n, H, DK, DV)).astype(np.float32)
+    S0[1] = 0.0                                   # a zero state
+    # a huge and a tiny key channel among the INT8 rows of every head (the
+    # FP16 rows hold the first 16 channels of each head's permutation)
+    int8 = [ch for ch in range(DK) if not any(ch in perm[h][:16] for h in range(H))]
+    S0[2, :, int8[0]] *= 2.0 ** 60
+    S0[2, :, int8[1]] *= 2.0 ** -60
+    gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    op = oracle.OraclePool(num_slots, H, perm, c)
+    ds = to_dev(slots, torch.int32)
+    gp.store(ds, to_dev(S0))
+    op.store(slots, S0)
+    kid = 0 if kind == "gdn" else 1
+    for t in range(steps):
+        d = _exact_inputs(r, n, H, kind)
+        case = t % 6
+        if case == 0:                             # full decay
+            if kind == "gdn":
+                d["gate"][:] = 0.0
+            else:
+                d["gate"][:] = -np.inf
+        elif case == 1:
+            d["beta"][:] = 0.0
+        elif case == 2:
+            d["k"][:] = 0.0
+        elif case == 3:
+            d["q"][:] = 0.0
+        elif case == 4:
+            d["v"][:] = 0.0
+        fn = gp.gdn_step if kind == "gdn" else gp.kda_step
+        og = fn(ds, to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), to_dev(d["gate"]),
+                to_dev(d["beta"])).cpu().numpy()
+        oo = op.decode_step(slots, d["q"], d["k"], d["v"], d["gate"], d["beta"], kid)
+        assert np.array_equal(og, oo), f"step {t} (case {case}): outputs differ"
+        assert_units_equal(split_gpu(gp, slots), oracle_units(op, slots), f"step {t} (case {case})")
+
+
 # ---------------------------------------------------------------------------
 # synthetic workloads with derived bounds
 # ---------------------------------------------------------------------------
