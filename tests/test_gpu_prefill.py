@@ -108,6 +108,43 @@ def test_prefill_fp32_pool_matches_exact(T, chunk, bf16, init):
     assert relS.max() <= REL_TOL, f"state rel err {relS.max():.3e}"
 
 
+@pytest.mark.parametrize("pool_fmt", ["fp32", "int8"])
+def test_prefill_degenerate_gates(pool_fmt):
+    """Tokens with alpha = 0 (the state is cleared; every decay ratio across
+    such a token is zero), alpha = 1, beta = 0 (no write) and a zero key,
+    inside chunks and on chunk boundaries: on an FP32 pool the readouts and
+    the final state match the exact recurrence; on a compressed pool each
+    chunk meets the oracle's bars."""
+    n, H, T, chunk, cfg = 2, 4, 150, 64, 3
+    perm = inputs.protected_perm(34, H)
+    c = inputs.smoothing(34, H, True)
+    d = inputs.prefill_inputs(cfg, n, H, T)
+    d["alpha"][:, [5, 63, 64, 100], :] = 0.0        # clears, one on each side of a chunk boundary
+    d["alpha"][:, 20:30, :] = 1.0
+    d["beta"][:, 40:44, :] = 0.0
+    d["k"][:, 80, :, :] = 0.0
+    d["alpha"][1, 110:, 2] = 0.0                   # one head cleared at every token of the last chunk
+    dev = _dev_inputs(d, False)
+    d = _as_seen(d, dev)
+    slots = np.array([1, 0], np.int32)
+    S0 = inputs.initial_state(34, n, H)
+    if pool_fmt == "int8":
+        run_chunkwise(n, H, T, chunk, False, perm, c, slots, S0, d, dev, sample=[0, 1])
+        return
+    gp = binding.StatePool(binding.FMT_FP32, 2, H, perm, c)
+    gp.store(to_dev(slots, torch.int32), to_dev(S0))
+    T0 = gp.dequant(to_dev(slots, torch.int32), binding.SPACE_STORED).cpu().numpy()
+    o = gp.prefill(to_dev(slots, torch.int32), dev["q"], dev["k"], dev["v"], dev["alpha"],
+                   dev["beta"], chunk=chunk, init_from_pool=True).cpu().numpy()
+    ox, Tx = _exact_chunk(T0.astype(np.float64), perm, c, d, 0, T)
+    rel = _rel_rows(o, ox)
+    assert rel.max() <= REL_TOL, f"readout rel err {rel.max():.3e} at {np.unravel_index(rel.argmax(), rel.shape)}"
+    Tg = gp.dequant(to_dev(slots, torch.int32), binding.SPACE_STORED).cpu().numpy()
+    relS = np.linalg.norm((Tg.reshape(n * H, -1) - Tx.reshape(n * H, -1)), axis=1) / \
+        np.linalg.norm(Tx.reshape(n * H, -1), axis=1)
+    assert relS.max() <= REL_TOL, f"state rel err {relS.max():.3e}"
+
+
 # ---------------------------------------------------------------------------
 # compressed pool
 # ---------------------------------------------------------------------------
