@@ -96,6 +96,56 @@ def test_windows_match_oracle(kind, cfg, window):
 
 
 @pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
+def test_window_degenerate_tokens(kind, cfg):
+    """Tokens inside a window with a full decay (alpha = 0, or g = -inf on
+    every channel), with beta = 0, with a zero key and with a zero query, and
+    a full decay at the window's last token: readouts and window-end states
+    against the oracle with the bars of test_windows_match_oracle."""
+    n, H, num_slots, window, windows = 4, 3, 6, 16, 2
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    slots = np.array([5, 0, 3, 1], np.int32)
+    ds = to_dev(slots, torch.int32)
+    gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    gp.store(ds, to_dev(inputs.initial_state(cfg, n, H)))
+    buf = gp.window_buffer(kind, window)
+    wo = oracle.OracleWindowPool(num_slots, H, perm, c, window)
+    kid = 0 if kind == "gdn" else 1
+    gate_key = "alpha" if kind == "gdn" else "g"
+    clear = 0.0 if kind == "gdn" else -np.inf
+    bound = StepBound(perm, c, kind)
+    t = 0
+    for w in range(windows):
+        _sync_oracle(wo, gp, slots)
+        T0 = dequant_units(*split_gpu(gp, slots))
+        toks = []
+        for j in range(window):
+            d = inputs.step_inputs(cfg, 500 + t, n, H, kind)
+            if j in (3, 11) or (w == 1 and j == window - 1):
+                d[gate_key][:] = clear          # every unit's state cleared at this token
+            if j == 6:
+                d["beta"][:] = 0.0
+            if j == 8:
+                d["k"][1] = 0.0
+            if j == 9:
+                d["q"][2] = 0.0
+            toks.append(d)
+            pos = np.full(n, j, np.int32)
+            og = gp.window_step(kind, window, buf, ds, to_dev(pos, torch.int32), to_dev(d["q"]),
+                                to_dev(d["k"]), to_dev(d["v"]), to_dev(d[gate_key]),
+                                to_dev(d["beta"])).cpu().numpy()
+            oo = wo.step(slots, pos, d["q"], d["k"], d["v"], d[gate_key], d["beta"], kid)
+            assert np.all(np.isfinite(og)), f"window {w} token {j}: non-finite readout"
+            err = np.abs(og - oo).max() / np.abs(oo).max()
+            assert err <= 1e-5, f"window {w} token {j}: readout error {err:.2e}"
+            t += 1
+        gu = split_gpu(gp, slots)
+        idx = (slots[:, None] * H + np.arange(H)[None, :]).ravel()
+        ou = (wo.pool.hi[idx], wo.pool.lo[idx], wo.pool.sc[idx])
+        _check_window_end(bound, gu, ou, T0, lambda b: toks, list(range(n)), H, f"window {w}")
+
+
+@pytest.mark.parametrize("kind,cfg", [("gdn", 1), ("kda", 2)])
 def test_mixed_positions_in_one_call(kind, cfg):
     """Slots join at different steps, so every call mixes tokens inside their
     windows with window ends (slot b at position (t - b) mod window).  Each
