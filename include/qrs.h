@@ -212,7 +212,8 @@ int qrs_decode_step_ex(qrs_pool pool, int kind, int io_dtype, const int32_t *slo
  * followed by qrs_kda_decode_step(pool, slots_kda, n_kda, ...) on the same
  * stream; on a QRS_FMT_I8F16 pool the two run in one kernel launch, which pays
  * the launch's ramp and drain once (small grids and the other formats make
- * the two calls).  Arguments of each group as for those calls (FP32, all
+ * the two calls), and deals each group's slots whole to the XCDs, which
+ * suits slots scattered over the pool; the results do not depend on it.  Arguments of each group as for those calls (FP32, all
  * heads); a group with n = 0 may pass NULL pointers.  A slot id in both groups
  * is undefined behaviour (the two updates of its units would race).
  * QRS_EINVAL: a NULL pool, a negative n, a NULL pointer of a non-empty group,
