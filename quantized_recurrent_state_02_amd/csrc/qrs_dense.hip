@@ -5,6 +5,8 @@
 // (HTML section 3.1, Eq.(1)), the same rows per thread (its columns are
 // interleaved, below) and the same stored coordinates; each unit is 65,536
 // bytes of FP32 read and written once.
+#include <atomic>
+
 #include "qrs_internal.h"
 
 namespace qrs {
@@ -13,11 +15,15 @@ namespace qrs {
 // 16 columns 32 j + 4 cb + i (j, i = 0..3): each 16-byte access of a wave
 // then covers 8 whole 128-byte row segments.  The unit is addressed through
 // a buffer resource (one 32-bit offset per lane), which keeps the kernel at
-// three waves per SIMD.
+// three waves per SIMD.  As in the compressed kernel, the first generation
+// of a grid of more than two generations starts staggered, here by j x 4096
+// cycles for the j-th workgroup on a CU (a unit is 3.2 times as many bytes):
+// 196.4-196.7 against 197.9-198.2 us at 8,192 units, 2 x 4096 within noise of
+// that, 2048 between (two passes each, alternating in one run).
 template <int KIND>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void
-decode_f32_kernel(PoolView pool, const int32_t *__restrict__ slots, int h0, int hc,
-                  const float *__restrict__ q, const float *__restrict__ k,
+decode_f32_kernel(PoolView pool, const int32_t *__restrict__ slots, int h0, int hc, int first_gen,
+                  int n_cus, const float *__restrict__ q, const float *__restrict__ k,
                   const float *__restrict__ v, const float *__restrict__ gate,
                   const float *__restrict__ beta, float *__restrict__ o) {
     __shared__ float s_k[DK];
@@ -32,6 +38,10 @@ decode_f32_kernel(PoolView pool, const int32_t *__restrict__ slots, int h0, int 
     __shared__ float4 red_w[16][DV / 4];
     __shared__ float4 red_z[16][DV / 4];
 
+    if ((int)blockIdx.x < first_gen) {
+        const int j = (int)blockIdx.x / n_cus;
+        for (int i = 0; i < j; ++i) __builtin_amdgcn_s_sleep(64);
+    }
     const int tid = threadIdx.x;
     const int H = pool.num_heads;
     const int b = blockIdx.x / hc;  // heads [h0, h0 + hc) of each slot
@@ -165,16 +175,44 @@ decode_f32_kernel(PoolView pool, const int32_t *__restrict__ slots, int h0, int 
     }
 }
 
+// Workgroups resident at launch (occupancy x CUs), queried once per device;
+// both kinds have the same resources.  Concurrent first calls may both query,
+// which is harmless (they store the same values).
+static void f32_residency(int *per_cu, int *cus) {
+    static std::atomic<int> s_per[16], s_cus[16];
+    *per_cu = 0;
+    *cus = 1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return;
+    int p = s_per[dev].load(std::memory_order_acquire);
+    int c = s_cus[dev].load(std::memory_order_relaxed);
+    if (p == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, decode_f32_kernel<0>, THREADS, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0 || p <= 0)
+            return;
+        s_cus[dev].store(c, std::memory_order_relaxed);
+        s_per[dev].store(p, std::memory_order_release);
+    }
+    *per_cu = p;
+    *cus = c;
+}
+
 hipError_t launch_decode_f32(int kind, const PoolView &pool, const int32_t *slots, int n, int h0,
                              int hc, const float *q, const float *k, const float *v,
                              const float *gate, const float *beta, float *o, hipStream_t stream) {
-    dim3 grid((unsigned)(n * hc)), block(THREADS);
+    int per_cu = 0, cus = 1;
+    f32_residency(&per_cu, &cus);
+    const int units = n * hc, resident = per_cu * cus;
+    const int first_gen = units > 2 * resident ? resident : 0;
+    dim3 grid((unsigned)units), block(THREADS);
     if (kind == 0)
-        hipLaunchKernelGGL(decode_f32_kernel<0>, grid, block, 0, stream, pool, slots, h0, hc, q, k,
-                           v, gate, beta, o);
+        hipLaunchKernelGGL(decode_f32_kernel<0>, grid, block, 0, stream, pool, slots, h0, hc,
+                           first_gen, cus, q, k, v, gate, beta, o);
     else
-        hipLaunchKernelGGL(decode_f32_kernel<1>, grid, block, 0, stream, pool, slots, h0, hc, q, k,
-                           v, gate, beta, o);
+        hipLaunchKernelGGL(decode_f32_kernel<1>, grid, block, 0, stream, pool, slots, h0, hc,
+                           first_gen, cus, q, k, v, gate, beta, o);
     return hipGetLastError();
 }
 
