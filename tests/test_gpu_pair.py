@@ -3,8 +3,10 @@ pool in one call) against the two separate calls, qrs_gdn_decode_step then
 qrs_kda_decode_step, which the decode tests check against the oracle: outputs
 and stored bytes equal bit for bit at every step.  Cases: a grid large enough
 for the one-launch kernel with its half-unit tail (and without the tail, whole
-units only), a small grid (the two calls), an empty group, and unknown slot
-ids in both groups."""
+units only), a small grid (the two calls), an empty group, unknown slot ids in
+both groups, head counts that are not powers of two (the kernel's XCD-aware
+order deals slots in runs of H heads), and the paged workload at full size in
+random and ascending slot order."""
 import numpy as np
 import pytest
 import torch
@@ -86,3 +88,51 @@ def test_pair_small_and_empty_groups(n_g, n_k):
 def test_pair_other_pool_formats(fmt):
     """On the other pool formats the pair call makes the two calls."""
     _run_both(4, 3, 2, 9, 2, 13, bad_g=1, fmt=fmt)
+
+
+@pytest.mark.parametrize("H,n_g,n_k", [(5, 110, 109), (12, 150, 150)])
+def test_pair_xcd_order_other_head_counts(H, n_g, n_k):
+    """The one-launch kernel deals each group's slots whole to the XCDs, in
+    runs of H heads: head counts that are not powers of two, a GDN group
+    whose unit count is not a multiple of 8 (so the KDA units start off an
+    XCD boundary), slots past the last full round of 8, and the half-unit
+    tail at 3,600 units, against the two calls bit for bit."""
+    _run_both(H, n_g, n_k, n_g + n_k + 3, 2, 21, bad_g=n_g - 1, bad_k=0)
+
+
+@pytest.mark.parametrize("order", ["random", "ascending"])
+def test_pair_full_paged_shape(order):
+    """The paged workload at full size, in the launch that the benchmark's
+    one-launch legs time: 4,096 slots x 32 heads, 512 GDN and 512 KDA
+    requests on distinct random slots (16,384 units per group, the KDA group
+    ending in the half-unit tail), in random slot order and in ascending
+    order.  One qrs_decode_step_pair call per step against the two calls on
+    a copy of the pool, outputs and every byte of the pool equal over three
+    steps."""
+    cfg, H, num_slots = 4, 32, 4096
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    gs, ks = inputs.paged_slots(cfg, num_slots, 1024)    # in random order
+    if order == "ascending":
+        gs, ks = np.sort(gs), np.sort(ks)
+    pa = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    pa.units().zero_()
+    active = np.concatenate([gs, ks]).astype(np.int32)
+    for i in range(0, len(active), 64):
+        S = inputs.initial_state_device(cfg, min(64, len(active) - i), H, perm, first=i)
+        pa.store(to_dev(active[i:i + 64], torch.int32), S)
+    pb = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    pb.units().copy_(pa.units())
+    dgs, dks = to_dev(gs, torch.int32), to_dev(ks, torch.int32)
+    for t in range(3):
+        dg = inputs.step_inputs_device(cfg, t, len(gs), H, "gdn")
+        dk = inputs.step_inputs_device(cfg, t, len(ks), H, "kda")
+        g_args = (dgs, dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"])
+        k_args = (dks, dk["q"], dk["k"], dk["v"], dk["g"], dk["beta"])
+        og_a, ok_a = pa.pair_step(g_args, k_args)
+        og_b = pb.gdn_step(*g_args)
+        ok_b = pb.kda_step(*k_args)
+        assert torch.equal(og_a.view(torch.int32), og_b.view(torch.int32)), f"step {t}: gdn outputs"
+        assert torch.equal(ok_a.view(torch.int32), ok_b.view(torch.int32)), f"step {t}: kda outputs"
+        assert bool(torch.isfinite(og_a).all()) and bool(torch.isfinite(ok_a).all())
+        assert torch.equal(pa.units(), pb.units()), f"step {t}: stored bytes differ"
