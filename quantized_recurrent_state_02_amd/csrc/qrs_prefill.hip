@@ -103,6 +103,29 @@ __device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStream));
 }
 
+// The masked, decayed tile: element (t, i) = r(t, i) acc for i < t (STRICT)
+// or i <= t, zero elsewhere; r as ratio() gives it.  Branch-free, with the
+// lane's log-prefix loads issued together: the lane's column i and its four
+// rows t.
+template <bool STRICT>
+__device__ __forceinline__ void gram_store(const PrefillSmem &s, float *dst, v4f acc, int tb,
+                                           int sb, int l16, int g) {
+    const int i = 16 * sb + l16;
+    const double li = s.lg[i];
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = expf((float)(s.lg[16 * tb + 4 * g + r] - li));
+    // all four are evaluated on every lane (no branch around each exp)
+    asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g + r;
+        const bool keep = STRICT ? (i < t) : (i <= t);
+        const float rt = s.zi[t] > i ? 0.f : e[r];   // ratio(s, t, i)
+        dst[t * LDM + i] = keep ? rt * acc[r] : 0.f;
+    }
+}
+
 // 16x16 tile of the masked Gram matrix  A[t][i] = r(t, i) * (X_t . K_i)  for
 // i < t (STRICT) or i <= t, zero elsewhere, rows t in [16 tb, +16), columns i
 // in [16 sb, +16); X = K or Q from LDS.  Written to dst (row stride LDM).
@@ -119,12 +142,7 @@ __device__ __forceinline__ void gram_tile(PrefillSmem &s, const float *X, float 
         acc = mfma4(a.z, b.z, acc);
         acc = mfma4(a.w, b.w, acc);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tb + 4 * g + r, i = 16 * sb + l16;
-        const bool keep = STRICT ? (i < t) : (i <= t);
-        dst[t * LDM + i] = keep ? ratio(s, t, i) * acc[r] : 0.f;
-    }
+    gram_store<STRICT>(s, dst, acc, tb, sb, l16, g);
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -161,12 +179,7 @@ __device__ __forceinline__ void gram_tile_bf16(PrefillSmem &s, const float *X, f
         const bf16x8 b = to_bf16x8(lds4(kb), lds4(kb + 4));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tb + 4 * g + r, i = 16 * sb + l16;
-        const bool keep = STRICT ? (i < t) : (i <= t);
-        dst[t * LDM + i] = keep ? ratio(s, t, i) * acc[r] : 0.f;
-    }
+    gram_store<STRICT>(s, dst, acc, tb, sb, l16, g);
 }
 
 }  // namespace
