@@ -457,14 +457,18 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         if (w == 0) {
             const int d = lane >> 4, j = lane & 15;
             const float *Md = s.M + 16 * d * LDM + 16 * d;
-            float y[16];
+            float bt[16], y[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) bt[t] = s.bet[16 * d + t];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 float acc = 0.f;
 #pragma unroll
                 for (int i = 0; i < t; ++i) acc = __builtin_fmaf(Md[t * LDM + i], y[i], acc);
-                const float bt = s.bet[16 * d + t];
-                y[t] = t < j ? 0.f : t == j ? bt : -bt * acc;
+                // every lane evaluates the row (no branch around it), so the
+                // next rows' reads can be issued early
+                asm volatile("" : "+v"(acc));
+                y[t] = t < j ? 0.f : t == j ? bt[t] : -bt[t] * acc;
             }
 #pragma unroll
             for (int t = 0; t < 16; ++t) s.Dinv[(16 * d + t) * LDI + j] = y[t];
@@ -504,7 +508,12 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             }
         }
 
-        // ---- 6. O = Gamma Q S0 + A_qk Delta, written as o = c (.) O ----
+        // ---- 6. O = Gamma Q S0 + A_qk Delta, written as o = c (.) O; the
+        //      output rows of the chunk through a buffer resource that ends at
+        //      its last real token (padding rows write nothing) ----
+        const int ostride = H * DV * 4;   // bytes between tokens
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(o + (((size_t)b * T + t0) * H + h) * DV, (ceff - 1) * ostride + DV * 4);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -534,12 +543,9 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tb + 4 * g + r;
-                if (t < ceff) {
-                    float *op = o + (((size_t)b * T + (t0 + t)) * H + h) * DV + 32 * w + l16;
-                    __builtin_nontemporal_store(c_out[0] * acc0[r], op);
-                    __builtin_nontemporal_store(c_out[1] * acc1[r], op + 16);
-                }
+                const int off = (16 * tb + 4 * g + r) * ostride + (32 * w + l16) * 4;
+                buf_storef(ro, c_out[0] * acc0[r], off, 0);
+                buf_storef(ro, c_out[1] * acc1[r], off + 64, 0);
             }
         }
 
