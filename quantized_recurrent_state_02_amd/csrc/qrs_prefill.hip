@@ -92,6 +92,18 @@ __device__ __forceinline__ float ratio(const PrefillSmem &s, int t, int i) {
     return expf((float)(s.lg[t] - s.lg[i]));
 }
 
+// a / b from y = RN(1/b): q = RN(a y) is within one ulp of a / b, the
+// residual a - b q is exact in one FMA, and RN(q + r y) is the correctly
+// rounded quotient (Markstein's theorem) unless a y or the residual falls
+// below the normal range, where it is within an ulp of it.  Three
+// instructions in place of the IEEE divide's ten; y is formed once per
+// column.
+__device__ __forceinline__ float div_by_recip(float a, float b, float y) {
+    const float q = a * y;
+    const float r = __builtin_fmaf(-b, q, a);
+    return __builtin_fmaf(r, y, q);
+}
+
 // One input element at byte offset off of a buffer (zero outside its range);
 // bf16 widens exactly to FP32.
 template <int IN_BF16>
@@ -355,11 +367,12 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
         // ---- 1. chunk operands into LDS (loaded during the previous chunk) ----
         const int lc = piece_col(), lt = piece_row();
         int inv_c[VPL];
-        float c_c[VPL];
+        float c_c[VPL], y_c[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             inv_c[i] = s.inv[lc + i];
             c_c[i] = pool.smooth[h * DV + lc + i];
+            y_c[i] = 1.0f / c_c[i];   // RN(1/c)
         }
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             for (int i = 0; i < VPL; ++i) {
                 s.K[t * LDK + inv_c[i]] = elem(kr4[j], i);
                 s.Q[t * LDK + inv_c[i]] = elem(qr4[j], i);
-                vv[i] = elem(vr4[j], i) / c_c[i];  // v' = D_c^{-1} v
+                vv[i] = div_by_recip(elem(vr4[j], i), c_c[i], y_c[i]);  // v' = D_c^{-1} v
             }
             // v' in model column order: whole 16-byte writes, each lane of a
             // 16-lane group on its own banks (single floats four columns apart
@@ -610,21 +623,54 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                         // INT8+Hadamard rows go through LDS (pass below)
                         F[(row - KHI) * LDK + c0] = v0;
                         F[(row - KHI) * LDK + c1] = v1;
-                    } else {
-                        const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
-                        const float sc = group_scale(amax);
+                    }
+                }
+            if (FMT == 1) {
+                // INT8 rows: each row's group maximum over its 16 lanes (the
+                // row16_max steps, each step taken for all 28 rows of the
+                // lane before the next, so no DPP read waits on the VALU
+                // write just before it), then scale, codes and the
+                // reconstruction the next chunk starts from
+                float m[7][4];
+#pragma unroll
+                for (int rb = 1; rb < 8; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        m[rb - 1][r] = fmaxf(fabsf(S[rb][0][r]), fabsf(S[rb][1][r]));
+#pragma unroll
+                for (int rb = 0; rb < 7; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0xb1>(m[rb][r]));
+#pragma unroll
+                for (int rb = 0; rb < 7; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0x4e>(m[rb][r]));
+#pragma unroll
+                for (int rb = 0; rb < 7; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0x141>(m[rb][r]));
+#pragma unroll
+                for (int rb = 0; rb < 7; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0x140>(m[rb][r]));
+                int8_t *cp = reinterpret_cast<int8_t *>(stg + LO_OFF);
+                const int c0 = 32 * w + l16, c1 = c0 + 16;
+#pragma unroll
+                for (int rb = 1; rb < 8; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int lr = 16 * rb + 4 * g + r - KHI;
+                        const float sc = group_scale(m[rb - 1][r]);
                         const double rinv = scale_reciprocal(sc);
-                        const float q0 = rintf(quant_quotient(v0, rinv));
-                        const float q1 = rintf(quant_quotient(v1, rinv));
-                        const int lr = row - KHI;
-                        int8_t *cp = reinterpret_cast<int8_t *>(stg + LO_OFF);
+                        const float q0 = rintf(quant_quotient(S[rb][0][r], rinv));
+                        const float q1 = rintf(quant_quotient(S[rb][1][r], rinv));
                         cp[lr * DV + c0] = (int8_t)(int)q0;
                         cp[lr * DV + c1] = (int8_t)(int)q1;
                         if (l16 == 0) reinterpret_cast<float *>(stg + SC_OFF)[lr * NGRP + w] = sc;
                         S[rb][0][r] = sc * q0;
                         S[rb][1][r] = sc * q1;
                     }
-                }
+            }
             __syncthreads();
             if (FMT == 2) {
                 // Each 32-value group on a lane pair, 16 values per lane (the
