@@ -92,6 +92,16 @@ __device__ __forceinline__ float ratio(const PrefillSmem &s, int t, int i) {
     return expf((float)(s.lg[t] - s.lg[i]));
 }
 
+// max(m, m of the lane that the DPP control CTRL names, inside the lane's
+// 16-lane row) for m the bits of a non-negative float (such floats order
+// like their bit patterns): one DPP-modified v_max_u32, with no
+// canonicalization of the operands as a float maximum would need.
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_max_step(uint32_t m) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, CTRL, 0xf, 0xf, true);
+    return m > o ? m : o;
+}
+
 // a / b from y = RN(1/b): q = RN(a y) is within one ulp of a / b, the
 // residual a - b q is exact in one FMA, and RN(q + r y) is the correctly
 // rounded quotient (Markstein's theorem) unless a y or the residual falls
@@ -631,28 +641,29 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
                 // lane before the next, so no DPP read waits on the VALU
                 // write just before it), then scale, codes and the
                 // reconstruction the next chunk starts from
-                float m[7][4];
+                uint32_t m[7][4];
 #pragma unroll
                 for (int rb = 1; rb < 8; ++rb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        m[rb - 1][r] = fmaxf(fabsf(S[rb][0][r]), fabsf(S[rb][1][r]));
+                        m[rb - 1][r] = __builtin_bit_cast(
+                            uint32_t, fmaxf(fabsf(S[rb][0][r]), fabsf(S[rb][1][r])));
 #pragma unroll
                 for (int rb = 0; rb < 7; ++rb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0xb1>(m[rb][r]));
+                    for (int r = 0; r < 4; ++r) m[rb][r] = row_max_step<0xb1>(m[rb][r]);
 #pragma unroll
                 for (int rb = 0; rb < 7; ++rb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0x4e>(m[rb][r]));
+                    for (int r = 0; r < 4; ++r) m[rb][r] = row_max_step<0x4e>(m[rb][r]);
 #pragma unroll
                 for (int rb = 0; rb < 7; ++rb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0x141>(m[rb][r]));
+                    for (int r = 0; r < 4; ++r) m[rb][r] = row_max_step<0x141>(m[rb][r]);
 #pragma unroll
                 for (int rb = 0; rb < 7; ++rb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m[rb][r] = fmaxf(m[rb][r], dpp_f<0x140>(m[rb][r]));
+                    for (int r = 0; r < 4; ++r) m[rb][r] = row_max_step<0x140>(m[rb][r]);
                 int8_t *cp = reinterpret_cast<int8_t *>(stg + LO_OFF);
                 const int c0 = 32 * w + l16, c1 = c0 + 16;
 #pragma unroll
@@ -660,7 +671,7 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int lr = 16 * rb + 4 * g + r - KHI;
-                        const float sc = group_scale(m[rb - 1][r]);
+                        const float sc = group_scale(__builtin_bit_cast(float, m[rb - 1][r]));
                         const double rinv = scale_reciprocal(sc);
                         const float q0 = rintf(quant_quotient(S[rb][0][r], rinv));
                         const float q1 = rintf(quant_quotient(S[rb][1][r], rinv));
