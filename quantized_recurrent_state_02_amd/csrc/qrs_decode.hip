@@ -287,7 +287,10 @@ __device__ __forceinline__ void decode_unit(
     const int rg2 = tid2 >> 3;
     const int off_hi2 = HI_OFF + rg2 * (DV * 2) + cb2 * 32;
     const int off_lo2 = rg2 * DV + cb2 * 16;
-    const int off_sc2 = (rg2 * NGRP + (cb2 >> 1)) * 4;
+    // The group's scale (or v1 metadata) is written by the even lane of the
+    // pair; the odd lane's offset lies past the unit's buffer range, so its
+    // store is dropped, with no branch around each row's store.
+    const int off_sc2 = (cb2 & 1) == 0 ? (rg2 * NGRP + (cb2 >> 1)) * 4 : kDropOffset;
     float bdc[COLS_PER_THREAD];
 #pragma unroll
     for (int c = 0; c < COLS_PER_THREAD; ++c) bdc[c] = s_bd[cb2 * 16 + c];
@@ -347,7 +350,7 @@ __device__ __forceinline__ void decode_unit(
             meta = __builtin_bit_cast(float, pr.meta);
         }
         buf_store16(st, cw, off_lo2, LO_OFF + 2048 * (r - 1));
-        if ((cb2 & 1) == 0) buf_storef(st, meta, off_sc2 + 256 * (r - 1), SC_OFF);
+        buf_storef(st, meta, off_sc2 + 256 * (r - 1), SC_OFF);
     }
 }
 

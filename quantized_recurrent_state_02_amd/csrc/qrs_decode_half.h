@@ -37,6 +37,9 @@
 
 namespace qrs {
 
+// A buffer offset past every resource range here: a store at it is dropped.
+constexpr int kDropOffset = 0x40000000;
+
 namespace half_unit {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -252,7 +255,7 @@ __device__ __forceinline__ void decode_half_unit(
     const int rg2 = tid2 >> 3;
     const int off_hi2 = HI_OFF + rg2 * (DV * 2) + (col0 + HCPT * cb2) * 2;
     const int off_lo2 = rg2 * DV + col0 + HCPT * cb2;
-    const int off_sc2 = (rg2 * NGRP + 2 * hf + (cb2 >> 2)) * 4;
+    const int off_sc2 = (cb2 & 3) == 0 ? (rg2 * NGRP + 2 * hf + (cb2 >> 2)) * 4 : kDropOffset;
     float bdc[HCPT];
 #pragma unroll
     for (int c = 0; c < HCPT; ++c) bdc[c] = s_bd[cb2 * HCPT + c];
@@ -285,7 +288,7 @@ __device__ __forceinline__ void decode_half_unit(
         cw.x = quant4(x[r][0], x[r][1], x[r][2], x[r][3], rinv);
         cw.y = quant4(x[r][4], x[r][5], x[r][6], x[r][7], rinv);
         buf_store8(st, cw, off_lo2, LO_OFF + 2048 * (r - 1));
-        if ((cb2 & 3) == 0) buf_storef(st, s, off_sc2 + 256 * (r - 1), SC_OFF);
+        buf_storef(st, s, off_sc2 + 256 * (r - 1), SC_OFF);
     }
 }
 
