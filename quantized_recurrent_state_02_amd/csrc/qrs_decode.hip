@@ -207,25 +207,44 @@ __device__ __forceinline__ void decode_unit(
 #pragma unroll
         for (int r = 1; r < ROWS_PER_THREAD; ++r) {
             const uint32_t m = __builtin_bit_cast(uint32_t, sc_old[r - 1]);
-            ok = ok && u8_group_exact(f16_bits_to_f32(m & 0xffffu), f16_bits_to_f32(m >> 16));
+            ok &= u8_group_exact(f16_bits_to_f32(m & 0xffffu), f16_bits_to_f32(m >> 16));
         }
         v1_int = __builtin_amdgcn_ballot_w64(!ok) == 0;
     }
+    // The row loop is written out once per path, so that the wave-uniform
+    // choice is one branch and each path one basic block (a choice inside
+    // the loop cut the rows apart: v1 tier 120.3 -> 117.7 us per step).
+    auto row_codes = [&](int r, uint32_t (&lw)[4]) {
+        lw[0] = lo_raw[r - 1].x;
+        lw[1] = lo_raw[r - 1].y;
+        lw[2] = lo_raw[r - 1].z;
+        lw[3] = lo_raw[r - 1].w;
+    };
+    if (CODEC == 0) {
 #pragma unroll
-    for (int r = 1; r < ROWS_PER_THREAD; ++r) {
-        const uint32_t lw[4] = {lo_raw[r - 1].x, lo_raw[r - 1].y, lo_raw[r - 1].z,
-                                lo_raw[r - 1].w};
-        if (CODEC == 1 && v1_int) {
+        for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+            uint32_t lw[4];
+            row_codes(r, lw);
+            const float a = dr[r] * sc_old[r - 1];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) x[r][c] = a * sext_byte_to_f32(lw[c >> 2], c & 3);
+        }
+    } else if (v1_int) {
+#pragma unroll
+        for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+            uint32_t lw[4];
+            row_codes(r, lw);
             const uint32_t m = __builtin_bit_cast(uint32_t, sc_old[r - 1]);
             const float sh = f16_bits_to_f32(m & 0xffffu), zh = f16_bits_to_f32(m >> 16);
             hadamard32_pair_codes(lw, sh, zh, (cb & 1) != 0, x[r]);
 #pragma unroll
             for (int c = 0; c < 16; ++c) x[r][c] = dr[r] * x[r][c];
-        } else if (CODEC == 0) {
-            const float a = dr[r] * sc_old[r - 1];
+        }
+    } else {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) x[r][c] = a * sext_byte_to_f32(lw[c >> 2], c & 3);
-        } else {
+        for (int r = 1; r < ROWS_PER_THREAD; ++r) {
+            uint32_t lw[4];
+            row_codes(r, lw);
             // reconstruct in the transformed domain, transform back, then decay
             const uint32_t m = __builtin_bit_cast(uint32_t, sc_old[r - 1]);
             const float sh = f16_bits_to_f32(m & 0xffffu), zh = f16_bits_to_f32(m >> 16);

@@ -223,7 +223,10 @@ __device__ __forceinline__ U8Params u8_params(float lo, float hi) {
     p.sh = f16_bits_to_f32(s16);
     p.rinv = scale_reciprocal(p.sh);
     const float z = rintf(quant_quotient(-lo, p.rinv));
-    const uint32_t z16 = p.sh == 0.0f ? 0u : f32_to_f16_bits(z);
+    // converted on every lane, then selected (no branch around it)
+    uint32_t z16 = f32_to_f16_bits(z);
+    asm volatile("" : "+v"(z16));
+    z16 = p.sh == 0.0f ? 0u : z16;
     p.zh = f16_bits_to_f32(z16);
     p.meta = s16 | (z16 << 16);
     return p;
