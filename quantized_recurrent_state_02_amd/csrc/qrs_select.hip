@@ -25,16 +25,42 @@ namespace qrs {
 namespace {
 
 constexpr int SEL_THREADS = 128;
+static_assert(SEL_THREADS == DK, "the error kernel's last step gives thread t row t");
+
+// max(m, m of the lane that the DPP control CTRL names, inside the lane's
+// 16-lane row), for m the bits of a non-negative float (such floats order
+// like their bit patterns): one DPP-modified v_max_u32.
+template <int CTRL>
+__device__ __forceinline__ uint32_t lane_max_step(uint32_t m) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, CTRL, 0xf, 0xf, true);
+    return m > o ? m : o;
+}
+
+// v from the lane that the DPP control CTRL names (inside the lane's 16-lane
+// row), for an FP64 value: its two halves moved separately.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xf, 0xf, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 // One workgroup per (sample, head).  Thread t works on row 4 p + (t >> 5) in
 // pass p (32 passes) and holds columns 4 (t & 31) .. +3; the eight threads of
-// one 32-value group are consecutive lanes.
+// one 32-value group are consecutive lanes, so the group maximum takes three
+// DPP steps (the partner in the pair, in the quad, in the eight lanes).  A
+// row's squared errors are summed over each 16-lane half of its 32 threads
+// with DPP (each step adds a lane and its partner in both orders, so the 16
+// lanes hold the same bits) and the two half sums go to LDS; at the end
+// thread t adds row t's two.
 __global__ __launch_bounds__(SEL_THREADS) void channel_error_kernel(
     const float *__restrict__ S, const float *__restrict__ smooth, int num_heads,
     double *__restrict__ e) {
     const int tid = threadIdx.x;
     const size_t sh = blockIdx.x;
     const int h = (int)(sh % (size_t)num_heads);
+    __shared__ double part[2][DK];   // the two half-row sums of each row
     const int rr = tid >> 5;
     const int l = tid & 31;
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(S + sh * (size_t)(DK * DV), DK * DV * 4);
@@ -65,8 +91,11 @@ __global__ __launch_bounds__(SEL_THREADS) void channel_error_kernel(
                 x[j] = quant_quotient(sv[j], rc[j]);  // stored value coordinates
                 amax = fmaxf(amax, fabsf(x[j]));
             }
-#pragma unroll
-            for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+            uint32_t mb = __builtin_bit_cast(uint32_t, amax);
+            mb = lane_max_step<0xb1>(mb);    // quad_perm [1,0,3,2]
+            mb = lane_max_step<0x4e>(mb);    // quad_perm [2,3,0,1]
+            mb = lane_max_step<0x141>(mb);   // row_half_mirror
+            amax = __builtin_bit_cast(float, mb);
             const float s = group_scale(amax);
             const double rinv = scale_reciprocal(s);
             double acc = 0.0;
@@ -77,11 +106,15 @@ __global__ __launch_bounds__(SEL_THREADS) void channel_error_kernel(
                 const double d = (double)back - (double)sv[j];
                 acc += d * d;
             }
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) acc += __shfl_xor(acc, off, 64);
-            if (l == 0) e[sh * DK + u] = acc;
+            acc += dpp_d<0xb1>(acc);    // quad_perm [1,0,3,2]
+            acc += dpp_d<0x4e>(acc);    // quad_perm [2,3,0,1]
+            acc += dpp_d<0x141>(acc);   // row_half_mirror
+            acc += dpp_d<0x140>(acc);   // row_mirror
+            if ((l & 15) == 0) part[l >> 4][u] = acc;
         }
     }
+    __syncthreads();
+    e[sh * DK + tid] = part[0][tid] + part[1][tid];
 }
 
 __device__ __forceinline__ bool sample_ok(int seq, int t, int n_seq, int T) {
