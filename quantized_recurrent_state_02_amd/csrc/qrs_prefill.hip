@@ -102,6 +102,19 @@ __device__ __forceinline__ uint32_t row_max_step(uint32_t m) {
     return m > o ? m : o;
 }
 
+// One step of the decay-prefix scans: la += la of the DPP source lane (0.0
+// where the lane has none), z = max(z, z of that lane) (-1 where none).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void scan_step(double &la, int &z) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, la);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xf, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xf, false);
+    const int zo = __builtin_amdgcn_update_dpp(-1, z, CTRL, ROWS, 0xf, false);
+    la += __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    z = max(z, zo);
+}
+
 // a / b from y = RN(1/b): q = RN(a y) is within one ulp of a / b, the
 // residual a - b q is exact in one FMA, and RN(q + r y) is the correctly
 // rounded quotient (Markstein's theorem) unless a y or the residual falls
@@ -408,15 +421,16 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             const float a = a_in;
             double la = a > 0.f ? log((double)a) : 0.0;
             int z = a > 0.f ? -1 : t;
-#pragma unroll
-            for (int off = 1; off < CT; off <<= 1) {
-                const double lo = __shfl_up(la, off, 64);
-                const int zo = __shfl_up(z, off, 64);
-                if (lane >= off) {
-                    la += lo;
-                    z = max(z, zo);
-                }
-            }
+            // inclusive scans over the 64 lanes with DPP: shifts by 1, 2, 4
+            // and 8 inside each 16-lane row, then lane 15 of a row into the
+            // next row and lane 31 into the upper half (the lanes without a
+            // source take the identity)
+            scan_step<0x111, 0xf>(la, z);   // row_shr:1
+            scan_step<0x112, 0xf>(la, z);   // row_shr:2
+            scan_step<0x114, 0xf>(la, z);   // row_shr:4
+            scan_step<0x118, 0xf>(la, z);   // row_shr:8
+            scan_step<0x142, 0xa>(la, z);   // row_bcast:15 into rows 1 and 3
+            scan_step<0x143, 0xc>(la, z);   // row_bcast:31 into rows 2 and 3
             s.lg[t] = la;
             s.zi[t] = z;
             s.gam[t] = z >= 0 ? 0.f : expf((float)la);
@@ -485,9 +499,16 @@ __global__ __launch_bounds__(PT) void prefill_kernel(PoolView pool, const int32_
             for (int t = 0; t < 16; ++t) bt[t] = s.bet[16 * d + t];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                float acc = 0.f;
+                // two interleaved partial sums halve the dependent chain
+                float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int i = 0; i < t; ++i) acc = __builtin_fmaf(Md[t * LDM + i], y[i], acc);
+                for (int i = 0; i < t; ++i) {
+                    if (i & 1)
+                        acc1 = __builtin_fmaf(Md[t * LDM + i], y[i], acc1);
+                    else
+                        acc0 = __builtin_fmaf(Md[t * LDM + i], y[i], acc0);
+                }
+                float acc = acc0 + acc1;
                 // every lane evaluates the row (no branch around it), so the
                 // next rows' reads can be issued early
                 asm volatile("" : "+v"(acc));
