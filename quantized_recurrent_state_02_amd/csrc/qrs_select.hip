@@ -137,24 +137,10 @@ __global__ __launch_bounds__(SEL_THREADS) void persistence_window_kernel(
         double p = 1.0;
         acc = 1.0;
         const int last = min(horizon, T - 1 - t);
-        const float *ap = a + (((size_t)seq * T + t) * num_heads + h) * DK + u;  // step t
-        const size_t step = (size_t)num_heads * DK;
-        // the decays of SEL_BATCH steps are loaded before any is used, so
-        // the loads overlap; the products and sums stay in step order
-        for (int j0 = 1; j0 <= last; j0 += SEL_BATCH) {
-            const int cnt = min(SEL_BATCH, last - j0 + 1);
-            float av[SEL_BATCH];
-            // past the window the index repeats its last step: every load is
-            // in range and none sits behind a branch
-#pragma unroll
-            for (int i = 0; i < SEL_BATCH; ++i) av[i] = ap[(size_t)(j0 + min(i, cnt - 1)) * step];
-#pragma unroll
-            for (int i = 0; i < SEL_BATCH; ++i)
-                if (i < cnt) {
-                    const double aj = (double)av[i];
-                    p = p * (aj * aj);
-                    acc = acc + p;
-                }
+        for (int j = 1; j <= last; ++j) {
+            const double aj = (double)a[(((size_t)seq * T + (t + j)) * num_heads + h) * DK + u];
+            p = p * (aj * aj);
+            acc = acc + p;
         }
     }
     W[sh * DK + u] = acc;
@@ -168,38 +154,16 @@ __global__ __launch_bounds__(SEL_THREADS) void persistence_geo_kernel(
     const int u = threadIdx.x;
     const int h = blockIdx.x;
     double L = 0.0;
-    bool bad = false;
-    // SEL_BATCH samples at a time: their decays loaded and their logs formed
-    // before the sum takes them in sample order
-    for (int s0 = 0; s0 < n && !bad; s0 += SEL_BATCH) {
-        const int cnt = min(SEL_BATCH, n - s0);
-        float av[SEL_BATCH];
-        // a sample past the end, of zero weight or out of range reads step 0
-        // of sequence 0 instead (always present), so no load sits behind a
-        // branch; such values are not used
-#pragma unroll
-        for (int i = 0; i < SEL_BATCH; ++i) {
-            const int si = s0 + min(i, cnt - 1);
-            const int seq = sample_seq[si], t = sample_t[si];
-            const bool use = weight[si] != 0.0 && sample_ok(seq, t, n_seq, T);
-            const size_t st = use ? (size_t)seq * T + t : 0;
-            av[i] = a[(st * num_heads + h) * DK + u];
+    for (int s = 0; s < n; ++s) {
+        const double w = weight[s];
+        if (w == 0.0) continue;
+        const int seq = sample_seq[s], t = sample_t[s];
+        if (!sample_ok(seq, t, n_seq, T)) {
+            L = __builtin_nan("");
+            break;
         }
-        double lg[SEL_BATCH];
-#pragma unroll
-        for (int i = 0; i < SEL_BATCH; ++i) lg[i] = log((double)av[i]);
-#pragma unroll
-        for (int i = 0; i < SEL_BATCH; ++i) {
-            if (i >= cnt || bad) continue;
-            const double w = weight[s0 + i];
-            if (w == 0.0) continue;
-            if (!sample_ok(sample_seq[s0 + i], sample_t[s0 + i], n_seq, T)) {
-                L = __builtin_nan("");
-                bad = true;
-                continue;
-            }
-            L = L + w * lg[i];
-        }
+        const double as = (double)a[(((size_t)seq * T + t) * num_heads + h) * DK + u];
+        L = L + w * log(as);
     }
     const double ae = exp(L);
     const double gap = 1.0 - ae * ae;
