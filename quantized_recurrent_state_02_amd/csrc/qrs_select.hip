@@ -147,24 +147,63 @@ __global__ __launch_bounds__(SEL_THREADS) void persistence_window_kernel(
 }
 
 // One workgroup per head, thread u = key channel.
-__global__ __launch_bounds__(SEL_THREADS) void persistence_geo_kernel(
+// Eight threads per key channel: in each pass the workgroup forms the terms
+// w_s log a_s of GEO_BATCH samples in parallel (thread part p takes samples
+// p, p + 8, ...) into LDS, then the channel's first thread adds them to its
+// sum in sample order, so the result is that of the one-thread loop.
+constexpr int GEO_PARTS = 8;
+constexpr int GEO_THREADS = GEO_PARTS * DK;
+constexpr int GEO_BATCH = 32;
+__global__ __launch_bounds__(GEO_THREADS) void persistence_geo_kernel(
     const float *__restrict__ a, int n_seq, int T, int num_heads, int n,
     const int32_t *__restrict__ sample_seq, const int32_t *__restrict__ sample_t,
     const double *__restrict__ weight, double tau, double *__restrict__ P) {
-    const int u = threadIdx.x;
+    __shared__ double term[GEO_BATCH][DK];
+    __shared__ int kind[GEO_BATCH];   // 0: skipped (zero weight, past n), 1: used, 2: out of range
+    const int u = threadIdx.x & (DK - 1);
+    const int part = threadIdx.x / DK;
     const int h = blockIdx.x;
     double L = 0.0;
-    for (int s = 0; s < n; ++s) {
-        const double w = weight[s];
-        if (w == 0.0) continue;
-        const int seq = sample_seq[s], t = sample_t[s];
-        if (!sample_ok(seq, t, n_seq, T)) {
-            L = __builtin_nan("");
-            break;
+    bool bad = false;
+    for (int s0 = 0; s0 < n; s0 += GEO_BATCH) {
+        const int cnt = min(GEO_BATCH, n - s0);
+        for (int i = part; i < GEO_BATCH; i += GEO_PARTS) {
+            int kd = 0;
+            double v = 0.0;
+            if (i < cnt) {
+                const int s = s0 + i;
+                const double w = weight[s];
+                const int seq = sample_seq[s], t = sample_t[s];
+                if (w != 0.0) {
+                    kd = sample_ok(seq, t, n_seq, T) ? 1 : 2;
+                    if (kd == 1)
+                        v = w * log((double)a[(((size_t)seq * T + t) * num_heads + h) * DK + u]);
+                }
+            }
+            term[i][u] = v;
+            if (u == 0) kind[i] = kd;
         }
-        const double as = (double)a[(((size_t)seq * T + t) * num_heads + h) * DK + u];
-        L = L + w * log(as);
+        __syncthreads();
+        if (part == 0) {
+            double tv[GEO_BATCH];
+            int kv[GEO_BATCH];
+#pragma unroll
+            for (int i = 0; i < GEO_BATCH; ++i) {
+                tv[i] = term[i][u];
+                kv[i] = kind[i];
+            }
+#pragma unroll
+            for (int i = 0; i < GEO_BATCH; ++i) {
+                if (kv[i] == 2 && !bad) {
+                    L = __builtin_nan("");
+                    bad = true;
+                }
+                if (kv[i] == 1 && !bad) L = L + tv[i];
+            }
+        }
+        __syncthreads();
     }
+    if (part != 0) return;
     const double ae = exp(L);
     const double gap = 1.0 - ae * ae;
     // fmax would drop a NaN gap (an out-of-range sample); keep it
@@ -223,7 +262,7 @@ hipError_t launch_persistence_geometric(int n_seq, int T, int num_heads, const f
                                         const int32_t *sample_seq, const int32_t *sample_t,
                                         const double *weight, double tau, double *P,
                                         hipStream_t stream) {
-    hipLaunchKernelGGL(persistence_geo_kernel, dim3((unsigned)num_heads), dim3(SEL_THREADS), 0,
+    hipLaunchKernelGGL(persistence_geo_kernel, dim3((unsigned)num_heads), dim3(GEO_THREADS), 0,
                        stream, a, n_seq, T, num_heads, n, sample_seq, sample_t, weight, tau, P);
     return hipGetLastError();
 }
