@@ -765,9 +765,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not "
-                                   "part of this build (decode units shard by slot or head "
-                                   "with no exchange)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; it has no multi-GPU "
+                                   "mode (decode units would shard by slot or head with no "
+                                   "exchange)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     # The oracle on one thread, in a child process started before this one

@@ -17,7 +17,7 @@ sums, the GPU FP32 with FMAs and a tree of partial sums):
   The readout differs by at most c_j sum_i |q_i| dx_ij plus 2^-20 c_j 130
   sum_i |q_i| |T_ij|.
 * The bar of one quantization step per stored element after N steps is
-  checked on the final state (north_star_step_ok): the two codes of an INT8
+  checked on the final state (one_step_ok): the two codes of an INT8
   element differ by at most one step wherever the group scales agree to
   rounding level and the last step's derived drift is below a step;
   everywhere, one step plus that derived drift, which the per-step bounds
@@ -107,7 +107,7 @@ class StepBound:
         return prop + eps
 
 
-def north_star_step_ok(Tg, To, sg, so, dx):
+def one_step_ok(Tg, To, sg, so, dx):
     """The bar of one quantization step per stored element.
 
     ``dx`` [..., 128, 128] is the derived bound on the difference of the two

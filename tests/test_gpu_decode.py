@@ -17,7 +17,7 @@ import torch
 import oracle
 from quantized_recurrent_state_02_amd import binding, inputs
 from tests.parity_util import (StepBound, assert_units_equal, dequant_units, describe_misses,
-                               north_star_step_ok, oracle_units, split_gpu, to_dev, ulp16)
+                               one_step_ok, oracle_units, split_gpu, to_dev, ulp16)
 
 pytestmark = pytest.mark.gpu
 DK = DV = 128
@@ -192,7 +192,7 @@ def run_parity(cfg, kind, n_gpu, H, steps, sample_slots, smooth):
                 ro = np.abs(og[bi, h] - oo[bi, h]) / lim_o
                 worst_out = max(worst_out, float(ro.max()))
                 assert ro.max() <= 1.0, f"step {t} unit {u}: readout outside derived bound"
-        ok_lo, ok_strict, ok_hi, _, st = north_star_step_ok(Tg, To, gu[2], ou[2], dxall)
+        ok_lo, ok_strict, ok_hi, _, st = one_step_ok(Tg, To, gu[2], ou[2], dxall)
         assert ok_strict.all(), (f"step {t}: {(~ok_strict).sum()} INT8 elements more than one "
                                  "step apart where the scales agree: "
                                  + describe_misses(ok_strict, Tg, To, gu[2], ou[2]))
@@ -201,7 +201,7 @@ def run_parity(cfg, kind, n_gpu, H, steps, sample_slots, smooth):
         D = Dn
     # final state: one quantization step (strictly where the scales agree to
     # rounding level), one step plus the last step's derived drift elsewhere
-    ok_lo, ok_strict, ok_hi, _, st = north_star_step_ok(Tg, To, gu[2], ou[2], dxall)
+    ok_lo, ok_strict, ok_hi, _, st = one_step_ok(Tg, To, gu[2], ou[2], dxall)
     assert ok_lo.all() and ok_hi.all() and ok_strict.all(), \
         (f"final state: {(~ok_lo).sum()} INT8 / {(~ok_hi).sum()} FP16 elements beyond the bound, "
          f"{(~ok_strict).sum()} beyond the strict step: "

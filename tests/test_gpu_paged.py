@@ -24,7 +24,7 @@ import torch
 
 import oracle
 from quantized_recurrent_state_02_amd import binding, inputs
-from tests.parity_util import (StepBound, dequant_units, describe_misses, north_star_step_ok,
+from tests.parity_util import (StepBound, dequant_units, describe_misses, one_step_ok,
                                oracle_units, split_gpu, to_dev, ulp16)
 
 pytestmark = pytest.mark.gpu
@@ -122,7 +122,7 @@ def test_paged_mixed_pool():
                 gu, ou = split_gpu(gp, sl), oracle_units(op, local[kind])
                 dxall, Tg, To = _check_step(kind, bounds[kind], sub, gu, ou, Tprev_o, D[kind])
                 checked += 1
-                ok_lo, ok_strict, ok_hi, _, st = north_star_step_ok(Tg, To, gu[2], ou[2], dxall)
+                ok_lo, ok_strict, ok_hi, _, st = one_step_ok(Tg, To, gu[2], ou[2], dxall)
                 assert ok_lo.all() and ok_hi.all() and ok_strict.all(), (
                     f"{kind} step {t}: {(~ok_lo).sum()} INT8 / {(~ok_hi).sum()} FP16 beyond the "
                     f"bound, {(~ok_strict).sum()} beyond the strict step: "

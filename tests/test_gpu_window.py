@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from quantized_recurrent_state_02_amd import binding, inputs
-from tests.parity_util import (StepBound, dequant_units, describe_misses, north_star_step_ok,
+from tests.parity_util import (StepBound, dequant_units, describe_misses, one_step_ok,
                                split_gpu, to_dev, window_end_bound)
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,7 @@ def _check_window_end(bound, gu, ou, T0, tokens_of, rows, H, what):
     for i, b in enumerate(rows):
         for h in range(H):
             dx[i * H + h] = window_end_bound(bound, T0[i * H + h], tokens_of(b), b, h)
-    ok_lo, ok_strict, ok_hi, _, st = north_star_step_ok(Tg, To, gu[2], ou[2], dx)
+    ok_lo, ok_strict, ok_hi, _, st = one_step_ok(Tg, To, gu[2], ou[2], dx)
     assert ok_lo.all() and ok_strict.all(), (
         f"{what}: {(~ok_lo).sum()} INT8 elements beyond the bound, {(~ok_strict).sum()} beyond "
         "the strict step: " + describe_misses(ok_lo & ok_strict, Tg, To, gu[2], ou[2]))
