@@ -90,13 +90,15 @@ def test_pair_other_pool_formats(fmt):
     _run_both(4, 3, 2, 9, 2, 13, bad_g=1, fmt=fmt)
 
 
-@pytest.mark.parametrize("H,n_g,n_k", [(5, 110, 109), (12, 150, 150)])
+@pytest.mark.parametrize("H,n_g,n_k", [(5, 110, 109), (12, 150, 150), (32, 16, 16), (32, 30, 34)])
 def test_pair_xcd_order_other_head_counts(H, n_g, n_k):
     """The one-launch kernel deals each group's slots whole to the XCDs, in
     runs of H heads: head counts that are not powers of two, a GDN group
     whose unit count is not a multiple of 8 (so the KDA units start off an
-    XCD boundary), slots past the last full round of 8, and the half-unit
-    tail at 3,600 units, against the two calls bit for bit."""
+    XCD boundary), slots past the last full round of 8, the half-unit tail
+    at 3,600 and 2,048 units (the smallest grid that takes it), and exactly
+    1,024 units (the smallest grid that takes the one-launch kernel),
+    against the two calls bit for bit."""
     _run_both(H, n_g, n_k, n_g + n_k + 3, 2, 21, bad_g=n_g - 1, bad_k=0)
 
 
