@@ -122,28 +122,106 @@ __device__ __forceinline__ bool sample_ok(int seq, int t, int n_seq, int T) {
     return seq >= 0 && seq < n_seq && t >= 0 && t < T;
 }
 
-// One workgroup per (sample, head), thread u = key channel.
-__global__ __launch_bounds__(SEL_THREADS) void persistence_window_kernel(
-    const float *__restrict__ a, int n_seq, int T, int num_heads,
+// One workgroup per block of PW_SAMPLES consecutive samples of the list and
+// one head, thread u = key channel.  Consecutive samples of one sequence
+// (a run) read overlapping stretches of its decays: the run's stretch is
+// staged through LDS PW_STEPS steps at a time, read from memory once, and
+// each sample of the run advances its own product and sum over its steps in
+// step order, so every result is the one-sample loop's.  A list in any
+// other order is still correct (runs of one sample).  PW_SPLIT threads per
+// channel take every PW_SPLIT-th sample, so that many chains run at once.
+constexpr int PW_SAMPLES = 16;
+constexpr int PW_STEPS = 64;
+constexpr int PW_SPLIT = 4;   // threads per channel, each taking every PW_SPLIT-th sample
+constexpr int PW_THREADS = PW_SPLIT * DK;
+__global__ __launch_bounds__(PW_THREADS) void persistence_window_kernel(
+    const float *__restrict__ a, int n_seq, int T, int num_heads, int n,
     const int32_t *__restrict__ sample_seq, const int32_t *__restrict__ sample_t, int horizon,
     double *__restrict__ W) {
-    const int u = threadIdx.x;
-    const size_t sh = blockIdx.x;
-    const size_t s = sh / (size_t)num_heads;
-    const int h = (int)(sh % (size_t)num_heads);
-    const int seq = sample_seq[s], t = sample_t[s];
-    double acc = __builtin_nan("");
-    if (sample_ok(seq, t, n_seq, T)) {
-        double p = 1.0;
-        acc = 1.0;
-        const int last = min(horizon, T - 1 - t);
-        for (int j = 1; j <= last; ++j) {
-            const double aj = (double)a[(((size_t)seq * T + (t + j)) * num_heads + h) * DK + u];
-            p = p * (aj * aj);
-            acc = acc + p;
+    __shared__ float stage[PW_STEPS][DK];
+    const int u = threadIdx.x & (DK - 1);
+    const int part = threadIdx.x / DK;
+    const int h = blockIdx.y;
+    const int s0 = blockIdx.x * PW_SAMPLES;
+    const int cnt = min(PW_SAMPLES, n - s0);
+    int seq[PW_SAMPLES], t[PW_SAMPLES], last[PW_SAMPLES];
+    double p[PW_SAMPLES], acc[PW_SAMPLES];
+#pragma unroll
+    for (int i = 0; i < PW_SAMPLES; ++i) {
+        seq[i] = -1;
+        t[i] = 0;
+        last[i] = 0;
+        if (i < cnt) {
+            seq[i] = sample_seq[s0 + i];
+            t[i] = sample_t[s0 + i];
+            if (!sample_ok(seq[i], t[i], n_seq, T)) seq[i] = -1;   // out of range: NaN
+            else last[i] = min(horizon, T - 1 - t[i]);
         }
+        p[i] = 1.0;
+        acc[i] = seq[i] >= 0 ? 1.0 : __builtin_nan("");
     }
-    W[sh * DK + u] = acc;
+    for (int i0 = 0; i0 < cnt;) {
+        int i1 = i0 + 1;
+        if (seq[i0] >= 0)
+            while (i1 < cnt && seq[i1] == seq[i0]) ++i1;
+        if (seq[i0] >= 0) {
+            // the run's steps: from the earliest sample's next step to the
+            // latest window end
+            int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+            for (int i = 0; i < PW_SAMPLES; ++i)
+                if (i >= i0 && i < i1) {
+                    lo = min(lo, t[i] + 1);
+                    hi = max(hi, t[i] + last[i]);
+                }
+            const float *as = a + ((size_t)seq[i0] * T * num_heads + h) * DK + u;  // step 0
+            const size_t step = (size_t)num_heads * DK;
+            for (int c0 = lo; c0 <= hi; c0 += PW_STEPS) {
+                const int nst = min(PW_STEPS, hi - c0 + 1);
+                float v[PW_STEPS / PW_SPLIT];
+                // the threads of a channel load alternate steps; past the
+                // stretch the index repeats its last step, so every load is
+                // in range and none sits behind a branch
+#pragma unroll
+                for (int j = 0; j < PW_STEPS / PW_SPLIT; ++j)
+                    v[j] = as[(size_t)(c0 + min(PW_SPLIT * j + part, nst - 1)) * step];
+                __syncthreads();   // the previous chunk has been read
+#pragma unroll
+                for (int j = 0; j < PW_STEPS / PW_SPLIT; ++j) stage[PW_SPLIT * j + part][u] = v[j];
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < PW_SAMPLES; ++i)
+                    if (i >= i0 && i < i1 && i % PW_SPLIT == part) {
+                        const int from = max(c0, t[i] + 1), to = min(c0 + nst - 1, t[i] + last[i]);
+                        double pi = p[i], ai = acc[i];
+                        int r = from;
+                        // eight steps' decays read before the chain takes them
+                        for (; r + 8 <= to + 1; r += 8) {
+                            float av[8];
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) av[k] = stage[r - c0 + k][u];
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) {
+                                const double aj = (double)av[k];
+                                pi = pi * (aj * aj);
+                                ai = ai + pi;
+                            }
+                        }
+                        for (; r <= to; ++r) {
+                            const double aj = (double)stage[r - c0][u];
+                            pi = pi * (aj * aj);
+                            ai = ai + pi;
+                        }
+                        p[i] = pi;
+                        acc[i] = ai;
+                    }
+            }
+        }
+        i0 = i1;
+    }
+#pragma unroll
+    for (int i = 0; i < PW_SAMPLES; ++i)
+        if (i < cnt && i % PW_SPLIT == part) W[((size_t)(s0 + i) * num_heads + h) * DK + u] = acc[i];
 }
 
 // One workgroup per head, thread u = key channel.
@@ -252,9 +330,10 @@ hipError_t launch_channel_error(int n, int num_heads, const float *S, const floa
 hipError_t launch_persistence_window(int n_seq, int T, int num_heads, const float *a, int n,
                                      const int32_t *sample_seq, const int32_t *sample_t,
                                      int horizon, double *W, hipStream_t stream) {
-    hipLaunchKernelGGL(persistence_window_kernel, dim3((unsigned)(n * num_heads)),
-                       dim3(SEL_THREADS), 0, stream, a, n_seq, T, num_heads, sample_seq, sample_t,
-                       horizon, W);
+    hipLaunchKernelGGL(persistence_window_kernel,
+                       dim3((unsigned)((n + PW_SAMPLES - 1) / PW_SAMPLES), (unsigned)num_heads),
+                       dim3(PW_THREADS), 0, stream, a, n_seq, T, num_heads, n, sample_seq,
+                       sample_t, horizon, W);
     return hipGetLastError();
 }
 
