@@ -63,6 +63,81 @@ __device__ __forceinline__ float lds_f32(const uint8_t *base, int byte_off) {
     return *reinterpret_cast<const float *>(base + byte_off);
 }
 
+// Calls of at most this many requests whose slots sit at different
+// positions of their windows run the requests at their window's last token
+// first.  Workgroups start in grid order, and a window-end token replays the
+// window and lives several times longer than the others: those started last
+// would set the end of the launch.  Longer calls keep the batch order.
+constexpr int ORDER_MAX = 1024;
+
+// The batch's positions as lane l holds them for ends_first_request:
+// positions 16 l .. 16 l + 15 (reads past the batch return zero).  Issued
+// before the unit's other loads, so that waiting for them waits for nothing
+// else.
+struct BatchPositions {
+    int v[16];
+};
+__device__ __forceinline__ BatchPositions load_positions(const int32_t *__restrict__ pos, int n) {
+    const int lane = __lane_id();
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(pos, min(n, ORDER_MAX) * 4);
+    BatchPositions bp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        bp.v[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(pr, (16 * lane + j) * 4, 0, 0);
+    return bp;
+}
+
+// The request that request rank r runs: the stable partition of the batch
+// into the requests at position `end` first and the rest after them, each
+// part in batch order (positions out of range count with the rest).  Lane l
+// holds positions 16 l .. 16 l + 15 (those past the batch are masked off);
+// the lanes' counts are prefix-summed from their five bit planes (a count is
+// at most 16) with one ballot and one lane count each; the lane whose range
+// holds the wanted request finds it among its 16 by halving.  Every wave
+// computes it from the same loads, so the result is wave-uniform.
+// 1 <= n <= ORDER_MAX.
+__device__ __forceinline__ int ends_first_request(const BatchPositions &bp, int n, int end, int r) {
+    const int lane = __lane_id();
+    const int nv = min(16, max(0, n - 16 * lane));   // this lane's positions in the batch
+    const uint32_t valid = (1u << nv) - 1u;
+    uint32_t m = 0;   // bit j: position 16 lane + j is at its window's end
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m |= (bp.v[j] == end ? 1u : 0u) << j;
+    m &= valid;
+    const int ce = __builtin_popcount(m);
+    int pre = 0, total = 0;   // ends before this lane's range, and in the batch
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t bm = __ballot((ce >> bit) & 1);
+        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))
+               << bit;
+        total += __popcll(bm) << bit;
+    }
+    const bool want_end = r < total;
+    const uint32_t mk = want_end ? m : (~m & valid);
+    const int cnt = want_end ? ce : nv - ce;
+    const int before = want_end ? pre : min(16 * lane, n) - pre;
+    const int t = (want_end ? r : r - total) - before;   // wanted request's index in this lane's part
+    const bool own = t >= 0 && t < cnt;
+    // the t-th set bit of mk
+    uint32_t mm = mk;
+    int k = t, at = 0;
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) {
+        const int c = __builtin_popcount(mm & ((1u << w) - 1u));
+        const bool up = k >= c;
+        k -= up ? c : 0;
+        mm = up ? mm >> w : mm;
+        at += up ? w : 0;
+    }
+    const uint64_t ob = __ballot(own);
+    int b = r;
+    if (ob != 0ull)
+        b = __builtin_amdgcn_readlane(16 * lane + at, (int)__builtin_ctzll(ob));
+    return min(b, n - 1);
+}
+
 }  // namespace
 
 template <int KIND>
@@ -75,7 +150,7 @@ template <int KIND>
 // 4% faster per token in phase than with two buffers.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void window_kernel(
     PoolView pool, uint8_t *__restrict__ buf, int window, const int32_t *__restrict__ slots,
-    const int32_t *__restrict__ pos, const float *__restrict__ q, const float *__restrict__ k,
+    const int32_t *__restrict__ pos, int n, const float *__restrict__ q, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ gate, const float *__restrict__ beta,
     float *__restrict__ o) {
     constexpr int R = window_record_bytes(KIND);
@@ -95,12 +170,36 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     extern __shared__ __align__(16) uint8_t s_rec[];  // this window's earlier records, (window - 1) * R bytes
 
     const int tid = threadIdx.x;
-    const int uu = blockIdx.x;
     const int H = pool.num_heads;
-    const int b = uu / H;
-    const int h = uu - b * H;
-    const int slot = slots[b];
-    const int p = pos[b];
+    const int rank = blockIdx.x / H;
+    const int h = blockIdx.x - rank * H;
+    // the request of the batch-order position is read with the three
+    // probes below and read again only where the partition moves the
+    // request; the partition's position loads are the first vector loads, so
+    // waiting for them waits for nothing else
+    int slot = slots[rank];
+    int p = pos[rank];
+    int b = rank;
+    // the partition only for a batch whose first, middle and last requests
+    // are not all at one position (a call with every slot in the same phase
+    // keeps the batch order without the scan); every workgroup decides from
+    // the same three entries, so all of them take the same order
+    const int p_first = pos[0], p_mid = pos[n >> 1], p_last = pos[n - 1];
+    if (n <= ORDER_MAX && (p_first != p_mid || p_first != p_last)) {
+        b = ends_first_request(load_positions(pos, n), n, window - 1, rank);
+        if (b != rank) {
+            slot = slots[b];
+            p = pos[b];
+        }
+    }
+    const size_t ob = ((size_t)b * H + h) * DK;
+    const float k_in = k[ob + tid];
+    const float v_in = v[ob + tid];
+    const float q_in = q[ob + tid];
+    const float beta_c = beta[b * H + h];
+    const float alpha_c = KIND == 0 ? gate[b * H + h] : 0.f;
+    const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
+    const int uu = b * H + h;   // the unit's output index
     if (slot < 0 || slot >= pool.num_slots || p < 0 || p >= window) {
         o[(size_t)uu * DV + tid] = __builtin_nanf("");
         return;
@@ -125,15 +224,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     U4 part[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) part[i] = buf_load16(rr, 16 * (tid + THREADS * i), 0);
-    const size_t ob = (size_t)uu * DK;
-    const float k_in = k[ob + tid];
-    const float v_in = v[ob + tid];
-    const float q_in = q[ob + tid];
     const float c_t = pool.smooth[h * DV + tid];
     const int perm_t = pool.perm[h * DK + tid];
-    const float beta_c = beta[uu];
-    const float alpha_c = KIND == 0 ? gate[uu] : 0.f;
-    const float g_c = KIND == 1 ? gate[ob + tid] : 0.f;
     // this token's decay of key channel tid as recorded (FP16), KDA
     const uint32_t lam16 = KIND == 1 ? decay_f16_bits(g_c) : 0u;
     const float lam_c = f16_bits_to_f32(lam16);
@@ -449,10 +541,10 @@ hipError_t launch_window(int kind, const PoolView &pool, uint8_t *buf, int windo
     const size_t lds = (size_t)(window - 1) * window_record_bytes(kind);
     if (kind == 0)
         hipLaunchKernelGGL(window_kernel<0>, grid, block, lds, stream, pool, buf, window, slots,
-                           pos, q, k, v, gate, beta, o);
+                           pos, n, q, k, v, gate, beta, o);
     else
         hipLaunchKernelGGL(window_kernel<1>, grid, block, lds, stream, pool, buf, window, slots,
-                           pos, q, k, v, gate, beta, o);
+                           pos, n, q, k, v, gate, beta, o);
     return hipGetLastError();
 }
 

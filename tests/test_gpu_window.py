@@ -197,6 +197,48 @@ def test_mixed_positions_in_one_call(kind, cfg):
     assert ends >= 2 * n - 2
 
 
+@pytest.mark.parametrize("kind,cfg,n", [("gdn", 1, 150), ("kda", 2, 150), ("gdn", 1, 1100)])
+def test_mixed_positions_many_requests(kind, cfg, n):
+    """Calls of up to 1,024 requests run the window-end requests first (the
+    kernel partitions the batch itself, 64 positions per ballot); longer calls
+    keep the batch order.  Here every call mixes all positions over more than
+    one ballot's worth of requests (150) and past the partitioned size (1,100),
+    with the slots in a shuffled order: each readout matches the oracle to
+    FP32 rounding, so every request ran once, on its own slot and records."""
+    H, window, steps = 1, 3, 7
+    rng = np.random.default_rng(5)
+    num_slots = n + 7
+    all_slots = rng.permutation(num_slots)[:n].astype(np.int32)
+    join = (np.arange(n) * 7) % window      # slot b starts its first window at step join[b]
+    perm = inputs.protected_perm(cfg, H)
+    c = inputs.smoothing(cfg, H, True)
+    gp = binding.StatePool(binding.FMT_I8F16, num_slots, H, perm, c)
+    gp.store(to_dev(all_slots, torch.int32), to_dev(inputs.initial_state(cfg, n, H)))
+    buf = gp.window_buffer(kind, window)
+    wo = oracle.OracleWindowPool(num_slots, H, perm, c, window)
+    kid = 0 if kind == "gdn" else 1
+    gate_key = "alpha" if kind == "gdn" else "g"
+    for t in range(steps):
+        active = np.flatnonzero(join <= t)
+        slots = all_slots[active]
+        pos = ((t - join[active]) % window).astype(np.int32)
+        starting = slots[pos == 0]
+        if len(starting):
+            _sync_oracle(wo, gp, starting)
+        d = inputs.step_inputs(cfg, t, n, H, kind)
+        args = [np.ascontiguousarray(d[x][active]) for x in ("q", "k", "v", gate_key, "beta")]
+        og = gp.window_step(kind, window, buf, to_dev(slots, torch.int32), to_dev(pos, torch.int32),
+                            *(to_dev(a) for a in args)).cpu().numpy()
+        oo = wo.step(slots, pos, *args, kid)
+        # the bar of the tests above (FP32 rounding relative to the call's
+        # largest readout), applied to each request's row
+        err = np.abs(og - oo).reshape(len(active), -1).max(axis=1) / np.abs(oo).max()
+        bad = np.flatnonzero(~(err <= 1e-5))
+        assert len(bad) == 0, (f"step {t}, {len(active)} requests: {len(bad)} readouts off, first at "
+                               f"batch rows {bad[:5].tolist()} (positions {pos[bad[:5]].tolist()}), "
+                               f"errors {err[bad[:5]].tolist()}")
+
+
 def test_invalid_position_and_slot():
     H, window = 2, 4
     gp = binding.StatePool(binding.FMT_I8F16, 3, H)
@@ -217,6 +259,17 @@ def test_invalid_position_and_slot():
     gp.window_step("gdn", window, buf, e32, e32, ez, ez, ez, eg, eg)
     torch.cuda.synchronize()
     assert torch.equal(gp.units(), before) and torch.equal(buf, buf_before)
+    # invalid requests among window ends and in-window tokens (a batch the
+    # kernel reorders, window ends first): NaN exactly on the invalid rows
+    gp2 = binding.StatePool(binding.FMT_I8F16, 5, H)
+    gp2.store(to_dev(np.arange(5, dtype=np.int32), torch.int32), to_dev(inputs.initial_state(1, 5, H)))
+    buf2 = gp2.window_buffer("gdn", window)
+    q5 = torch.randn((5, H, DK), device="cuda")
+    g5 = torch.full((5, H), 0.5, device="cuda")
+    o = gp2.window_step("gdn", window, buf2, to_dev(np.array([0, 1, 9, 2, 3], np.int32), torch.int32),
+                        to_dev(np.array([window, window - 1, window - 1, 0, window - 1], np.int32),
+                               torch.int32), q5, q5, q5, g5, g5).cpu()
+    assert torch.isnan(o[[0, 2]]).all() and torch.isfinite(o[[1, 3, 4]]).all()
     with pytest.raises(binding.QrsError, match="UNSUPPORTED"):
         binding.StatePool(binding.FMT_U8H16, 3, H).window_step(
             "gdn", window, buf, ds, to_dev(np.zeros(3, np.int32), torch.int32), q, q, q, g, g)
