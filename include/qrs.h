@@ -251,10 +251,12 @@ int qrs_decode_step_pair(qrs_pool pool, const int32_t *slots_gdn, int n_gdn, con
  *     outputs.
  * q, k, v, o: FP32 [n][H][128] as for the other decode calls.
  * Scheduling: the window's last token replays the window's updates and takes
- * several times longer than the others.  For n <= 1024 the kernel runs the
- * requests at position window - 1 first and the rest after them, each part in
- * batch order; longer calls run in batch order, where listing the window-end
- * requests first has the same effect.  The results do not depend on the order.
+ * several times longer than the others.  When n <= 1024 and the first, middle
+ * and last requests (pos[0], pos[n / 2], pos[n - 1]) are not all at one
+ * position, the kernel runs the requests at position window - 1 first and the
+ * rest after them, each part in batch order; other calls run in batch order,
+ * where listing the window-end requests first has the same effect.  The
+ * results do not depend on the order.
  * QRS_EUNSUPPORTED on other pool formats.
  */
 size_t qrs_window_buffer_bytes(int kind, int num_slots, int num_heads, int window);
