@@ -879,7 +879,8 @@ def main():
                                      warm_s=leg_warm)
             window_res["staggered_ends_first"] = {
                 "workload": "the same staggered phases, the batch ordered by descending window "
-                            "position at every step (window-end requests first in the grid)",
+                            "position at every step (the caller listing the window-end requests first, "
+                            "the order the kernel itself gives a mixed call)",
                 "us_per_step": sec_e * 1e6, "updates_per_s": n * H / sec_e,
                 "gbs": n * H * BYTES_GDN_WINDOW / sec_e / 1e9,
                 "frac_of_peak": n * H * BYTES_GDN_WINDOW / sec_e / 1e9 / PEAK_HBM_GBS,
