@@ -197,14 +197,15 @@ def test_mixed_positions_in_one_call(kind, cfg):
     assert ends >= 2 * n - 2
 
 
-@pytest.mark.parametrize("kind,cfg,n", [("gdn", 1, 150), ("kda", 2, 150), ("gdn", 1, 1100)])
+@pytest.mark.parametrize("kind,cfg,n", [("gdn", 1, 150), ("kda", 2, 150), ("gdn", 1, 1024), ("gdn", 1, 1100)])
 def test_mixed_positions_many_requests(kind, cfg, n):
-    """Calls of up to 1,024 requests run the window-end requests first (the
-    kernel partitions the batch itself, 64 positions per ballot); longer calls
-    keep the batch order.  Here every call mixes all positions over more than
-    one ballot's worth of requests (150) and past the partitioned size (1,100),
-    with the slots in a shuffled order: each readout matches the oracle to
-    FP32 rounding, so every request ran once, on its own slot and records."""
+    """Calls of up to 1,024 requests at mixed positions run the window-end
+    requests first (the kernel partitions the batch itself, 16 positions per
+    lane of a wave); longer calls keep the batch order.  Here the calls mix
+    all positions over several lanes' ranges (150), over all 64 lanes (1,024,
+    the largest partitioned call) and past the partitioned size (1,100), with
+    the slots in a shuffled order: each readout matches the oracle to FP32
+    rounding, so every request ran once, on its own slot and records."""
     H, window, steps = 1, 3, 7
     rng = np.random.default_rng(5)
     num_slots = n + 7
