@@ -26,7 +26,6 @@ namespace {
 
 constexpr int SEL_THREADS = 128;
 static_assert(SEL_THREADS == DK, "the error kernel's last step gives thread t row t");
-constexpr int SEL_BATCH = 16;   // loads in flight per thread in the serial kernels
 
 // max(m, m of the lane that the DPP control CTRL names, inside the lane's
 // 16-lane row), for m the bits of a non-negative float (such floats order
@@ -224,28 +223,37 @@ __global__ __launch_bounds__(PW_THREADS) void persistence_window_kernel(
         if (i < cnt && i % PW_SPLIT == part) W[((size_t)(s0 + i) * num_heads + h) * DK + u] = acc[i];
 }
 
-// One workgroup per head, thread u = key channel.
-// Eight threads per key channel: in each pass the workgroup forms the terms
-// w_s log a_s of GEO_BATCH samples in parallel (thread part p takes samples
-// p, p + 8, ...) into LDS, then the channel's first thread adds them to its
-// sum in sample order, so the result is that of the one-thread loop.
-constexpr int GEO_PARTS = 8;
-constexpr int GEO_THREADS = GEO_PARTS * DK;
-constexpr int GEO_BATCH = 32;
-__global__ __launch_bounds__(GEO_THREADS) void persistence_geo_kernel(
+// The geometric persistence and the scores: one workgroup per head and block
+// of SUM_CH key channels (DK / SUM_CH workgroups per head), SUM_PARTS
+// threads per channel.  In each pass the workgroup forms the terms of
+// SUM_BATCH samples (thread part p takes samples p, p + SUM_PARTS, ...) into
+// one of two LDS buffers, and the channel's first thread adds them to its sum
+// in sample order while the others form the next pass's terms in the other
+// buffer, so each sum is that of the one-thread loop over the samples.
+constexpr int SUM_CH = 16;
+constexpr int SUM_PARTS = 64;
+constexpr int SUM_THREADS = SUM_CH * SUM_PARTS;
+constexpr int SUM_BATCH = 128;
+constexpr int SUM_PER = SUM_BATCH / SUM_PARTS;   // terms per thread and pass
+static_assert(DK % SUM_CH == 0 && SUM_BATCH % SUM_PARTS == 0, "summation tiling");
+
+__global__ __launch_bounds__(SUM_THREADS) void persistence_geo_kernel(
     const float *__restrict__ a, int n_seq, int T, int num_heads, int n,
     const int32_t *__restrict__ sample_seq, const int32_t *__restrict__ sample_t,
     const double *__restrict__ weight, double tau, double *__restrict__ P) {
-    __shared__ double term[GEO_BATCH][DK];
-    __shared__ int kind[GEO_BATCH];   // 0: skipped (zero weight, past n), 1: used, 2: out of range
-    const int u = threadIdx.x & (DK - 1);
-    const int part = threadIdx.x / DK;
-    const int h = blockIdx.x;
+    __shared__ double term[2][SUM_BATCH][SUM_CH];
+    __shared__ int kind[2][SUM_BATCH];   // 0: skipped (zero weight), 1: used, 2: out of range
+    const int ul = threadIdx.x & (SUM_CH - 1);
+    const int part = threadIdx.x / SUM_CH;
+    const int h = blockIdx.x / (DK / SUM_CH);
+    const int u = (blockIdx.x % (DK / SUM_CH)) * SUM_CH + ul;
     double L = 0.0;
     bool bad = false;
-    for (int s0 = 0; s0 < n; s0 += GEO_BATCH) {
-        const int cnt = min(GEO_BATCH, n - s0);
-        for (int i = part; i < GEO_BATCH; i += GEO_PARTS) {
+    for (int s0 = 0, pass = 0; s0 < n; s0 += SUM_BATCH, pass ^= 1) {
+        const int cnt = min(SUM_BATCH, n - s0);
+#pragma unroll
+        for (int j = 0; j < SUM_PER; ++j) {
+            const int i = part + SUM_PARTS * j;
             int kd = 0;
             double v = 0.0;
             if (i < cnt) {
@@ -258,28 +266,31 @@ __global__ __launch_bounds__(GEO_THREADS) void persistence_geo_kernel(
                         v = w * log((double)a[(((size_t)seq * T + t) * num_heads + h) * DK + u]);
                 }
             }
-            term[i][u] = v;
-            if (u == 0) kind[i] = kd;
+            term[pass][i][ul] = v;
+            if (ul == 0) kind[pass][i] = kd;
         }
+        // this pass's terms are in; the pass before last has been summed
+        // (its buffer is the one written above)
         __syncthreads();
         if (part == 0) {
-            double tv[GEO_BATCH];
-            int kv[GEO_BATCH];
+            for (int i0 = 0; i0 < cnt; i0 += 8) {
+                double tv[8];
+                int kv[8];
 #pragma unroll
-            for (int i = 0; i < GEO_BATCH; ++i) {
-                tv[i] = term[i][u];
-                kv[i] = kind[i];
-            }
-#pragma unroll
-            for (int i = 0; i < GEO_BATCH; ++i) {
-                if (kv[i] == 2 && !bad) {
-                    L = __builtin_nan("");
-                    bad = true;
+                for (int q = 0; q < 8; ++q) {
+                    tv[q] = term[pass][min(i0 + q, SUM_BATCH - 1)][ul];
+                    kv[q] = i0 + q < cnt ? kind[pass][min(i0 + q, SUM_BATCH - 1)] : 0;
                 }
-                if (kv[i] == 1 && !bad) L = L + tv[i];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (kv[q] == 2 && !bad) {
+                        L = __builtin_nan("");
+                        bad = true;
+                    }
+                    if (kv[q] == 1 && !bad) L = L + tv[q];
+                }
             }
         }
-        __syncthreads();
     }
     if (part != 0) return;
     const double ae = exp(L);
@@ -288,32 +299,50 @@ __global__ __launch_bounds__(GEO_THREADS) void persistence_geo_kernel(
     P[(size_t)h * DK + u] = gap != gap ? gap : 1.0 / fmax(gap, tau);
 }
 
-// One workgroup per head, thread u = key channel.
-__global__ __launch_bounds__(SEL_THREADS) void channel_scores_kernel(
+// Scores: term w_s e_s (times W_s for the window persistence), summed in
+// sample order, times P for the geometric one.  The summation tiling above.
+__global__ __launch_bounds__(SUM_THREADS) void channel_scores_kernel(
     int n, int num_heads, const double *__restrict__ e, const double *__restrict__ W,
     const double *__restrict__ P, const double *__restrict__ weight, double *__restrict__ C) {
-    const int u = threadIdx.x;
-    const int h = blockIdx.x;
+    __shared__ double term[2][SUM_BATCH][SUM_CH];
+    const int ul = threadIdx.x & (SUM_CH - 1);
+    const int part = threadIdx.x / SUM_CH;
+    const int h = blockIdx.x / (DK / SUM_CH);
+    const int u = (blockIdx.x % (DK / SUM_CH)) * SUM_CH + ul;
     double acc = 0.0;
-    // SEL_BATCH samples' operands loaded before the sum takes them in order
-    for (int s0 = 0; s0 < n; s0 += SEL_BATCH) {
-        const int cnt = min(SEL_BATCH, n - s0);
-        double ev[SEL_BATCH], wv[SEL_BATCH];
+    for (int s0 = 0, pass = 0; s0 < n; s0 += SUM_BATCH, pass ^= 1) {
+        const int cnt = min(SUM_BATCH, n - s0);
+        double ev[SUM_PER], wv[SUM_PER], wt[SUM_PER];
         // past the last sample the index repeats it: no load behind a branch
 #pragma unroll
-        for (int j = 0; j < SEL_BATCH; ++j) {
-            const size_t i = ((size_t)(s0 + min(j, cnt - 1)) * num_heads + h) * DK + u;
-            ev[j] = e[i];
-            wv[j] = W ? W[i] : 1.0;
+        for (int j = 0; j < SUM_PER; ++j) {
+            const int sm = s0 + min(part + SUM_PARTS * j, cnt - 1);
+            const size_t idx = ((size_t)sm * num_heads + h) * DK + u;
+            ev[j] = e[idx];
+            wv[j] = W ? W[idx] : 1.0;
+            wt[j] = weight[sm];
         }
 #pragma unroll
-        for (int j = 0; j < SEL_BATCH; ++j)
-            if (j < cnt) {
-                double term = weight[s0 + j] * ev[j];
-                if (W) term = term * wv[j];
-                acc = acc + term;
+        for (int j = 0; j < SUM_PER; ++j) {
+            double t = wt[j] * ev[j];
+            if (W) t = t * wv[j];
+            term[pass][part + SUM_PARTS * j][ul] = t;
+        }
+        // this pass's terms are in; the pass before last has been summed
+        // (its buffer is the one written above)
+        __syncthreads();
+        if (part == 0) {
+            for (int i0 = 0; i0 < cnt; i0 += 8) {
+                double tv[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) tv[q] = term[pass][min(i0 + q, SUM_BATCH - 1)][ul];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (i0 + q < cnt) acc = acc + tv[q];
             }
+        }
     }
+    if (part != 0) return;
     if (P) acc = acc * P[(size_t)h * DK + u];
     C[(size_t)h * DK + u] = acc;
 }
@@ -341,7 +370,8 @@ hipError_t launch_persistence_geometric(int n_seq, int T, int num_heads, const f
                                         const int32_t *sample_seq, const int32_t *sample_t,
                                         const double *weight, double tau, double *P,
                                         hipStream_t stream) {
-    hipLaunchKernelGGL(persistence_geo_kernel, dim3((unsigned)num_heads), dim3(GEO_THREADS), 0,
+    hipLaunchKernelGGL(persistence_geo_kernel, dim3((unsigned)(num_heads * (DK / SUM_CH))),
+                       dim3(SUM_THREADS), 0,
                        stream, a, n_seq, T, num_heads, n, sample_seq, sample_t, weight, tau, P);
     return hipGetLastError();
 }
@@ -349,7 +379,8 @@ hipError_t launch_persistence_geometric(int n_seq, int T, int num_heads, const f
 hipError_t launch_channel_scores(int n, int num_heads, const double *e, const double *W,
                                  const double *P, const double *weight, double *C,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(channel_scores_kernel, dim3((unsigned)num_heads), dim3(SEL_THREADS), 0,
+    hipLaunchKernelGGL(channel_scores_kernel, dim3((unsigned)(num_heads * (DK / SUM_CH))),
+                       dim3(SUM_THREADS), 0,
                        stream, n, num_heads, e, W, P, weight, C);
     return hipGetLastError();
 }
