@@ -83,6 +83,36 @@ def test_persistence_and_scores_match_oracle():
     assert np.array_equal(Cp, sel.channel_scores(e, w, P=Po))
 
 
+def test_persistence_and_scores_many_samples():
+    """300 samples: the window kernel's blocks of 16 samples (runs of one
+    sequence inside a block, and runs cut by block edges), and the summation
+    kernels' passes of 128 samples through both LDS buffers and a partial last
+    pass; zero weights skip their samples.  Window and scores bit for bit, the
+    geometric persistence to the oracle's rounding of the logarithms."""
+    n_seq, T, H, horizon, n = 4, 64, 3, 20, 300
+    rng = np.random.default_rng(11)
+    a = _traj_decays(9, n_seq, T, H)
+    seqs = np.sort(rng.integers(0, n_seq, n)).astype(np.int32)
+    seqs[::7] = rng.integers(0, n_seq, len(seqs[::7]))    # some runs broken up
+    ts = rng.integers(0, T, n).astype(np.int32)
+    w = sel.domain_weights(rng.integers(0, 3, n))
+    w[rng.choice(n, 25, replace=False)] = 0.0
+    da, ds, dt = to_dev(a), to_dev(seqs, torch.int32), to_dev(ts, torch.int32)
+    dw = to_dev(w, torch.float64)
+    Wg = binding.persistence_window(da, ds, dt, horizon).cpu().numpy()
+    Wo = sel.persistence_window(a, seqs, ts, horizon)
+    assert np.array_equal(Wg, Wo)
+    Pg = binding.persistence_geometric(da, ds, dt, dw, 1e-4).cpu().numpy()
+    Po = sel.persistence_geometric(a, seqs, ts, w, 1e-4)
+    assert np.allclose(Pg, Po, rtol=1e-14, atol=0)
+    e = np.abs(rng.normal(0, 1, (n, H, DK)))
+    de = to_dev(e, torch.float64)
+    Cw = binding.channel_scores(de, dw, W=to_dev(Wo, torch.float64)).cpu().numpy()
+    assert np.array_equal(Cw, sel.channel_scores(e, w, W=Wo))
+    Cp = binding.channel_scores(de, dw, P=to_dev(Po, torch.float64)).cpu().numpy()
+    assert np.array_equal(Cp, sel.channel_scores(e, w, P=Po))
+
+
 def test_invalid_sample_gives_nan():
     a = _traj_decays(1, 2, 8, 2)
     W = binding.persistence_window(to_dev(a), to_dev(np.array([0, 2], np.int32), torch.int32),
